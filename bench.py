@@ -1,0 +1,251 @@
+"""Benchmark of the routed fused-MoE expert FFN on one MI355X.
+
+One step = one forward of the routed kernel (gate/up into the fp16 hidden
+workspace, then down with the routed-weight scale) over one batch of
+synthetic, already packed, HBM-resident inputs with prebuilt tables -- the
+"routed_kernel_only" timing scope of the benchmark write-up
+("MetaX-TileLang工具链", section 1.12.2).  Contract building, packing and
+allocation are outside the timed region.
+
+Prints ONE JSON line.  value = useful TFLOP/s = 6*pairs*H*I / step time.
+roofline: the dominant kernel (gate/up) against HBM (decode-shaped) or
+dense fp16 MFMA (prefill-shaped) peak, its launch duration measured with HIP
+events recorded on the stream the kernels run on.  cpu_baseline: the oracle
+timed on the host cores on a bounded sample of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
+METRIC = "fused MoE TFLOP/s (useful 6·pairs·H·I) + % MFMA/HBM roofline, 1×MI355X"
+KERNEL_SOURCES = {"gate_up": ["rmoe_stream.hip", "rmoe_tile.hip", "rmoe_device.h"],
+                  "down": ["rmoe_stream.hip", "rmoe_tile.hip", "rmoe_device.h"]}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode",
+                    help="tiny | decode | prefill | fine | large (default: decode)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "stream", "tile"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_src_hash(which: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[which]:
+        with open(os.path.join(ROOT, "mixture_experts_routed_grouped_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stats_ms(xs):
+    s = sorted(xs)
+    q = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
+    return {"mean": statistics.fmean(s), "median": q(0.5), "p90": q(0.9), "p99": q(0.99),
+            "min": s[0], "std": statistics.pstdev(s)}
+
+
+def algorithmic(cfg, c, variant):
+    """Algorithmic bytes and useful flops per launch of each kernel.
+
+    gate/up: both weight matrices of every expert that has rows, the valid
+    token rows, the hidden rows written.  down: the down weights of every
+    active expert, the hidden rows read, the out rows written, the routed
+    weights.  Padding rows and empty experts move nothing."""
+    import numpy as np
+    H, I = cfg.hidden, cfg.intermediate
+    pairs = c["pairs"]
+    e_act = int(np.count_nonzero(np.asarray(c["group_sizes"])))
+    gu_bytes = 2 * e_act * I * H * 2 + pairs * H * 2 + pairs * I * 2
+    dn_bytes = e_act * H * I * 2 + pairs * I * 2 + pairs * H * 2 + pairs * 4
+    return {"gate_up": {"bytes": gu_bytes, "flops": 4.0 * pairs * H * I},
+            "down": {"bytes": dn_bytes, "flops": 2.0 * pairs * H * I},
+            "experts_active": e_act}
+
+
+def traffic_for(kernel: str, workload: str):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter
+    summary, only if the kernel sources have not changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_src_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """Time the oracle (as it stands) on a bounded sample of rows of the same
+    workload, on every host core OpenMP gets; scale to TFLOP/s of useful
+    work."""
+    import numpy as np
+    from oracle import ref
+    nt = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    k = cfg.top_k
+    ids = inp.topk_ids
+    # sample: pairs spread over the routing, in pair order
+    pairs_all = np.arange(ids.size)
+    experts = sorted({int(e) for e in ids.reshape(-1)[:64]})
+    host = {}
+
+    def rows_for(sel):
+        xs, gl, ul, dl, ws = [], [], [], [], []
+        for p in sel:
+            t, j = divmod(int(p), k)
+            e = int(ids[t][j])
+            if e not in host:
+                host[e] = (inp.wg[e].cpu().numpy(), inp.wu[e].cpu().numpy(), inp.wd[e].cpu().numpy())
+            xs.append(x_host[t])
+            gl.append(host[e][0])
+            ul.append(host[e][1])
+            dl.append(host[e][2])
+            ws.append(float(inp.topk_w[t][j]))
+        return xs, gl, ul, dl, ws
+
+    x_host = inp.x.cpu().numpy()
+    # calibrate with one row per thread, then size the sample to ~target_s
+    sel = pairs_all[:nt]
+    args = rows_for(sel)
+    t0 = time.perf_counter()
+    ref.moe_rows(*args, n_threads=nt)
+    t_cal = time.perf_counter() - t0
+    n_rounds = max(1, int(target_s / max(t_cal, 1e-6)))
+    n_rows = min(len(pairs_all), nt * n_rounds)
+    sel = pairs_all[:n_rows]
+    args = rows_for(sel)
+    t0 = time.perf_counter()
+    ref.moe_rows(*args, n_threads=nt)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * n_rows * cfg.hidden * cfg.intermediate
+    del experts
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
+            "sample": f"{n_rows} of {ids.size} routed rows (first in pair order), full H and I; "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this routed-kernel build has no multi-GPU path "
+              "(expert/tensor sharding is a design note, not code). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_grouped_amd as R
+    import workloads
+
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.make_inputs(cfg, device=dev)
+    c = R.build_contract(inp.topk_ids, cfg.experts)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    gs, go, gpo, gidx = (i32(c[k]) for k in ["group_sizes", "group_offsets",
+                                             "group_padded_offsets", "group_idx_for_bx"])
+    prow, cpos = i32(c["padded_row_of_pair"]), i32(c["compact_pos_of_pair"])
+    Tp, H, I, E = c["total_padded_tokens"], cfg.hidden, cfg.intermediate, cfg.experts
+    stacked = torch.zeros((Tp, H), dtype=torch.float16, device=dev)
+    w_compact = torch.zeros(c["pairs"], dtype=torch.float32, device=dev)
+    topk_w = torch.from_numpy(inp.topk_w.reshape(-1).copy()).to(dev)
+    R.pack(inp.x, topk_w, prow, cpos, stacked, w_compact)
+    hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
+    out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
+    variant = args.variant
+    resolved = variant if variant != "auto" else ("stream" if c["pairs"] <= 48 * E else "tile")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        R.gate_up(stacked, inp.wg, inp.wu, gs, gpo, gidx, hid, variant=resolved)
+        if evs is not None:
+            evs[1].record()
+        R.down(hid, inp.wd, w_compact, gs, go, gpo, gidx, out, variant=resolved)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    alg = algorithmic(cfg, c, resolved)
+    useful = cfg.useful_flops()
+    value = useful / (ms_per_step * 1e-3) / 1e12
+    gu_s = statistics.fmean(gu_ms) * 1e-3
+    dn_s = statistics.fmean(dn_ms) * 1e-3
+    hbm_bound = resolved == "stream"
+    if hbm_bound:
+        ach = alg["gate_up"]["bytes"] / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS}
+    else:
+        ach = alg["gate_up"]["flops"] / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_F16_TFLOPS}
+    roof["kernel"] = "gate_up (" + ("stream_kernel<true,4>" if hbm_bound else "tile_kernel<true>") + ")"
+    roof["traffic"] = traffic_for("gate_up", cfg.name)
+    total_bytes = alg["gate_up"]["bytes"] + alg["down"]["bytes"]
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens, E={E}, top_k={cfg.top_k}, "
+                               f"H={H}, I={I}, {cfg.routing} routing, seed {cfg.seed}",
+                   "tokens": cfg.tokens, "experts": E, "top_k": cfg.top_k, "hidden": H,
+                   "intermediate": I, "pairs": c["pairs"], "num_blocks_m": c["num_blocks_m"],
+                   "experts_active": alg["experts_active"], "scope": "routed_kernel_only",
+                   "variant": resolved},
+        "roofline": roof,
+        "step_hbm_gbs": total_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_hbm_frac": total_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "step_mfma_frac": value / PEAK_F16_TFLOPS,
+        "kernels": {
+            "gate_up": {"avg_us": gu_s * 1e6, "alg_bytes": alg["gate_up"]["bytes"],
+                        "gbs": alg["gate_up"]["bytes"] / gu_s / 1e9,
+                        "tflops": alg["gate_up"]["flops"] / gu_s / 1e12},
+            "down": {"avg_us": dn_s * 1e6, "alg_bytes": alg["down"]["bytes"],
+                     "gbs": alg["down"]["bytes"] / dn_s / 1e9,
+                     "tflops": alg["down"]["flops"] / dn_s / 1e12},
+        },
+        "latency_ms": stats_ms(step_ms),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

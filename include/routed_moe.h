@@ -1,0 +1,201 @@
+/*
+ * routed_moe.h -- C ABI of the MI355X (gfx950) routed fused-MoE expert FFN.
+ *
+ * What the library computes, for every expert-sorted token row r of a
+ * 128-row block bx whose expert is e = group_idx_for_bx[bx]
+ * ("Fused MoE GEMM 提交说明", sections 算子来源 and 完整算子代码):
+ *
+ *     gate   = x[r] . gate_w[e]^T              fp16 x fp16, fp32 accumulation
+ *     up     = x[r] . up_w[e]^T
+ *     hidden = fp16( silu(gate) * up )         written to the fp16 workspace
+ *     out[r] = fp16( (hidden . down_w[e]^T) * routed_expert_weights[c] )
+ *
+ * with token_offset = bx*128 - group_padded_offsets[e],
+ * actual_rows = max(0, min(128, group_sizes[e] - token_offset)),
+ * row r = bx*128 + i for i < actual_rows, and the COMPACT index
+ * c = group_offsets[e] + token_offset + i (section 实现要点: tokens, the
+ * workspace and out use padded rows, routed weights use compact rows).
+ * Rows i >= actual_rows (padding) are neither computed nor written, in out
+ * and in the workspace alike.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (RMOE_OK) on success, a negative rmoe_status otherwise; no
+ *     exception crosses the ABI.  On an error nothing is launched.
+ *   - Tensors are row-major and contiguous.  "device" pointers are HIP
+ *     device memory owned by the caller; "host" pointers are host memory
+ *     owned by the caller.  The library keeps no pointer after returning.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t
+ *     passed as void*; NULL is the default stream).  Nothing synchronises,
+ *     nothing allocates, and no table is read back to the host: the tables'
+ *     contents are a precondition (check them with rmoe_validate_contract).
+ *     A device fault shows at the caller's next synchronisation.
+ *   - fp16 is IEEE binary16 (passed as void*), fp32 is float, tables int32.
+ */
+#ifndef ROUTED_MOE_H
+#define ROUTED_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMOE_API __attribute__((visibility("default")))
+
+/* Rows per block: the kernel's block_token and the contract's padding_M. */
+#define RMOE_BLOCK_M 128
+
+typedef enum rmoe_status {
+    RMOE_OK = 0,
+    RMOE_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad count */
+    RMOE_ERR_UNSUPPORTED_SHAPE = -2, /* hidden/intermediate not a multiple of 128, ... */
+    RMOE_ERR_MISALIGNED = -3,        /* a tensor pointer not 16-byte aligned */
+    RMOE_ERR_LAUNCH = -4,            /* the HIP runtime refused a launch */
+    RMOE_ERR_CONTRACT = -5,          /* tables violate the dispatch contract */
+    RMOE_ERR_CAPACITY = -6           /* an output table is too small */
+} rmoe_status;
+
+/* Kernel family for the forward (RMOE_VARIANT_AUTO picks by shape). */
+#define RMOE_VARIANT_AUTO 0
+#define RMOE_VARIANT_STREAM 1 /* few rows per block: weight streaming, split K */
+#define RMOE_VARIANT_TILE 2   /* many rows per block: LDS-tiled MFMA GEMM */
+
+/* Human-readable name of a status code (static storage). */
+RMOE_API const char *rmoe_status_str(int status);
+
+/* Library version string (static storage). */
+RMOE_API const char *rmoe_version(void);
+
+/*
+ * Host-side dispatch contract (tutorial page "moe_dispatch_contract.py",
+ * build_contract steps 1-4; padding rule ceil((count+1)/128)*128).
+ *   topk_ids [num_tokens, top_k] host int32, each in [0, num_experts).
+ *   Pair p = t*top_k + j.  Pairs are sorted by expert, stably (ties keep
+ *   ascending p).
+ * Outputs (host, caller-allocated):
+ *   group_sizes [E]; group_offsets [E+1] (exclusive scan, last = pairs);
+ *   group_padded_offsets [E+1] (scan of padded spans, multiples of 128);
+ *   group_idx_for_bx [capacity_blocks] filled for bx < *num_blocks_m, where
+ *   *num_blocks_m = ceil(pairs/128) + E and block bx belongs to the last
+ *   expert whose padded start is <= bx*128;
+ *   order [pairs] (the sorted pair ids); padded_row_of_pair [pairs]
+ *   (the token row in the padded layout); compact_pos_of_pair [pairs]
+ *   (the routed-weight index).  order/padded/compact may be NULL.
+ * Errors: RMOE_ERR_INVALID_ARGUMENT for an id out of range or a bad size,
+ * RMOE_ERR_CAPACITY when capacity_blocks < ceil(pairs/128) + E.
+ */
+RMOE_API int rmoe_build_contract(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                                 int32_t num_experts, int32_t *group_sizes,
+                                 int32_t *group_offsets, int32_t *group_padded_offsets,
+                                 int32_t *group_idx_for_bx, int64_t capacity_blocks,
+                                 int32_t *num_blocks_m, int32_t *order,
+                                 int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair);
+
+/*
+ * Check host copies of the tables against the contract (the tutorial's three
+ * self-checks in their strict form): offsets start at 0 and step by the
+ * sizes, padded spans are (size/128 + 1)*128, group_idx_for_bx is the block
+ * -> expert map, every padded interval fits in num_blocks_m*128 <=
+ * total_padded_tokens, and group_offsets[E] == total_valid_tokens.
+ * Returns RMOE_OK or RMOE_ERR_CONTRACT.
+ */
+RMOE_API int rmoe_validate_contract(const int32_t *group_sizes, const int32_t *group_offsets,
+                                    const int32_t *group_padded_offsets,
+                                    const int32_t *group_idx_for_bx, int32_t num_experts,
+                                    int32_t num_blocks_m, int64_t total_padded_tokens,
+                                    int64_t total_valid_tokens);
+
+/* Bytes of the fp16 hidden workspace: total_padded_tokens * intermediate * 2. */
+RMOE_API size_t rmoe_workspace_bytes(int64_t total_padded_tokens, int64_t intermediate);
+
+/*
+ * The fused expert FFN forward (the submission's run_kernel, with the
+ * workspace passed in as the runtime-level call does).
+ *   stacked_expert_tokens [Tp, H] fp16 device, expert-sorted, 128-padded;
+ *   gate_w, up_w [E, I, H] fp16 device; down_w [E, H, I] fp16 device;
+ *   routed_expert_weights [pairs] fp32 device, compact order;
+ *   group_sizes [E], group_offsets [E+1], group_padded_offsets [E+1],
+ *   group_idx_for_bx [num_blocks_m]: int32 device;
+ *   workspace [Tp, I] fp16 device (rmoe_workspace_bytes); out [Tp, H] fp16
+ *   device.  Only valid rows of workspace and out are written.
+ *   H = hidden, I = intermediate (multiples of 128), E = num_experts >= 1,
+ *   Tp = total_padded_tokens >= num_blocks_m*128, pairs = total_valid_tokens.
+ * Two kernels are enqueued on `stream`: gate/up into the workspace, then
+ * down into out.
+ */
+RMOE_API int rmoe_forward_f16(const void *stacked_expert_tokens, const void *gate_w,
+                              const void *up_w, const void *down_w,
+                              const float *routed_expert_weights, const int32_t *group_sizes,
+                              const int32_t *group_offsets, const int32_t *group_padded_offsets,
+                              const int32_t *group_idx_for_bx, void *workspace, void *out,
+                              int64_t hidden, int64_t intermediate, int32_t num_experts,
+                              int64_t total_padded_tokens, int64_t total_valid_tokens,
+                              int32_t num_blocks_m, void *stream);
+
+/* rmoe_forward_f16 with an explicit kernel family (RMOE_VARIANT_*). */
+RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const void *gate_w,
+                                      const void *up_w, const void *down_w,
+                                      const float *routed_expert_weights,
+                                      const int32_t *group_sizes, const int32_t *group_offsets,
+                                      const int32_t *group_padded_offsets,
+                                      const int32_t *group_idx_for_bx, void *workspace,
+                                      void *out, int64_t hidden, int64_t intermediate,
+                                      int32_t num_experts, int64_t total_padded_tokens,
+                                      int64_t total_valid_tokens, int32_t num_blocks_m,
+                                      int32_t variant, void *stream);
+
+/*
+ * Stage 1 alone (the Step-1 grid of section 完整算子代码): workspace rows =
+ * fp16(silu(x.Wg^T) * (x.Wu^T)) for valid rows.  Arguments as above.
+ */
+RMOE_API int rmoe_gate_up_f16(const void *stacked_expert_tokens, const void *gate_w,
+                              const void *up_w, const int32_t *group_sizes,
+                              const int32_t *group_padded_offsets,
+                              const int32_t *group_idx_for_bx, void *workspace, int64_t hidden,
+                              int64_t intermediate, int32_t num_experts,
+                              int64_t total_padded_tokens, int32_t num_blocks_m,
+                              int32_t variant, void *stream);
+
+/*
+ * Stage 2 alone (the Step-2 grid): out rows = fp16((hidden.Wd^T) * w[c])
+ * for valid rows, reading the workspace written by stage 1.
+ */
+RMOE_API int rmoe_down_f16(const void *workspace, const void *down_w,
+                           const float *routed_expert_weights, const int32_t *group_sizes,
+                           const int32_t *group_offsets, const int32_t *group_padded_offsets,
+                           const int32_t *group_idx_for_bx, void *out, int64_t hidden,
+                           int64_t intermediate, int32_t num_experts,
+                           int64_t total_padded_tokens, int64_t total_valid_tokens,
+                           int32_t num_blocks_m, int32_t variant, void *stream);
+
+/*
+ * Token packing (the benchmark write-up "MetaX-TileLang工具链", section
+ * 1.12.1/2.7: grouping tokens by expert before the routed kernel):
+ *   stacked[padded_row_of_pair[p]] = x[p / top_k]            (fp16 rows of H)
+ *   w_compact[compact_pos_of_pair[p]] = topk_weights[p]      (fp32)
+ * for p < num_tokens*top_k.  x [num_tokens, H] fp16 device, topk_weights
+ * [num_tokens*top_k] fp32 device, maps int32 device, stacked [Tp, H] fp16
+ * device, w_compact [pairs] fp32 device.  Other rows of stacked are not
+ * written.  H must be a multiple of 8.
+ */
+RMOE_API int rmoe_pack_f16(const void *x, const float *topk_weights,
+                           const int32_t *padded_row_of_pair, const int32_t *compact_pos_of_pair,
+                           int64_t num_tokens, int32_t top_k, int64_t hidden, void *stacked,
+                           float *w_compact, int64_t total_padded_tokens, void *stream);
+
+/*
+ * Combine (same write-up, section 2.7 item 7: the scatter-reduce of the k
+ * expert outputs of each token): y[t] = fp16( sum_j out[padded_row_of_pair
+ * [t*top_k + j]] ) with the sum in fp32 in slot order j = 0..top_k-1.
+ * out [Tp, H] fp16 device, y [num_tokens, H] fp16 device.  H multiple of 8.
+ */
+RMOE_API int rmoe_combine_f16(const void *out, const int32_t *padded_row_of_pair,
+                              int64_t num_tokens, int32_t top_k, int64_t hidden, void *y,
+                              int64_t total_padded_tokens, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTED_MOE_H */

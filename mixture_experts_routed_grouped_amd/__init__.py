@@ -1,0 +1,276 @@
+"""Routed fused-MoE expert FFN for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``librmoe.so`` (declared in ``include/routed_moe.h``)
+with the same entry-point names.  It only marshals arguments: torch tensors
+become device pointers plus the current HIP stream, numpy arrays become host
+pointers.  Every step of the routed path runs in the library's HIP kernels
+or its C++ host code; if the library is missing, importing works but every
+call raises ``RmoeError`` -- there is no fallback.
+
+The submission-style entry point ``run_kernel`` keeps the argument order of
+"Fused MoE GEMM 提交说明" (section 提交文件) and, like that template, caches
+the fp16 hidden workspace per (device, rows, intermediate).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librmoe.so")
+
+BLOCK_M = 128
+VARIANT_AUTO, VARIANT_STREAM, VARIANT_TILE = 0, 1, 2
+_VARIANTS = {"auto": 0, "stream": 1, "tile": 2, 0: 0, 1: 1, 2: 2}
+
+
+class RmoeError(RuntimeError):
+    pass
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64, _I32 = ctypes.c_int64, ctypes.c_int32
+
+_SIGS = {
+    "rmoe_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "rmoe_version": ([], ctypes.c_char_p),
+    "rmoe_build_contract": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "rmoe_validate_contract": ([_P, _P, _P, _P, _I32, _I32, _I64, _I64], ctypes.c_int),
+    "rmoe_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "rmoe_forward_f16": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
+    "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
+                                 ctypes.c_int),
+    "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I32, _I32, _P], ctypes.c_int),
+    "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
+    "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
+    "rmoe_combine_f16": ([_P, _P, _I64, _I32, _I64, _P, _I64, _P], ctypes.c_int),
+}
+
+
+def lib():
+    """The loaded library; raises RmoeError if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RmoeError(f"{LIB_PATH} is missing: build it with "
+                            "`python mixture_experts_routed_grouped_amd/build_lib.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().rmoe_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise RmoeError(f"{what}: {status_str(status)} ({status})")
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+# ------------------------------------------------------------- host contract
+def build_contract(topk_ids, num_experts: int) -> dict:
+    """Dispatch tables for a routing ``topk_ids`` [T, k] (host int32), built
+    by the library's C++ contract builder.  Returns numpy int32 arrays."""
+    ids = np.ascontiguousarray(np.asarray(topk_ids, dtype=np.int32))
+    if ids.ndim != 2:
+        raise ValueError("topk_ids must be [num_tokens, top_k]")
+    T, k = ids.shape
+    E = int(num_experts)
+    pairs = T * k
+    M_cap = -(-pairs // BLOCK_M) + E
+    gs = np.zeros(E, np.int32)
+    go = np.zeros(E + 1, np.int32)
+    gpo = np.zeros(E + 1, np.int32)
+    gidx = np.zeros(max(M_cap, 1), np.int32)
+    M = np.zeros(1, np.int32)
+    order = np.zeros(max(pairs, 1), np.int32)
+    prow = np.zeros(max(pairs, 1), np.int32)
+    cpos = np.zeros(max(pairs, 1), np.int32)
+    st = lib().rmoe_build_contract(_np_ptr(ids), T, k, E, _np_ptr(gs), _np_ptr(go), _np_ptr(gpo),
+                                   _np_ptr(gidx), M_cap, _np_ptr(M), _np_ptr(order), _np_ptr(prow),
+                                   _np_ptr(cpos))
+    _check(st, "rmoe_build_contract")
+    M = int(M[0])
+    return {
+        "n_experts": E,
+        "pairs": pairs,
+        "group_sizes": gs,
+        "group_offsets": go,
+        "group_padded_offsets": gpo,
+        "num_blocks_m": M,
+        "group_idx_for_bx": gidx[:M].copy(),
+        "order": order[:pairs].copy(),
+        "padded_row_of_pair": prow[:pairs].copy(),
+        "compact_pos_of_pair": cpos[:pairs].copy(),
+        "total_padded_tokens": M * BLOCK_M,
+    }
+
+
+def validate_contract(group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx,
+                      num_experts, num_blocks_m, total_padded_tokens, total_valid_tokens) -> int:
+    """Returns the library status (0 = the tables satisfy the contract)."""
+    arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.int32)) for a in
+            (group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx)]
+    return int(lib().rmoe_validate_contract(*[_np_ptr(a) for a in arrs], int(num_experts),
+                                            int(num_blocks_m), int(total_padded_tokens),
+                                            int(total_valid_tokens)))
+
+
+def workspace_bytes(total_padded_tokens: int, intermediate: int) -> int:
+    return int(lib().rmoe_workspace_bytes(int(total_padded_tokens), int(intermediate)))
+
+
+# ------------------------------------------------------------- device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live in GPU memory")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+
+
+def forward(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
+            group_offsets, group_padded_offsets, group_idx_for_bx, workspace, out,
+            variant="auto", stream=None):
+    """Enqueue the fused expert FFN (gate/up then down) on ``stream`` (default:
+    the current stream).  Shapes: tokens [Tp, H], gate/up [E, I, H], down
+    [E, H, I] fp16; routed weights [pairs] fp32; tables int32; workspace
+    [Tp, I] and out [Tp, H] fp16.  Asynchronous; writes only valid rows."""
+    torch = _torch()
+    x = stacked_expert_tokens
+    E, I, H = gate_w.shape
+    Tp = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != H or tuple(up_w.shape) != (E, I, H) or \
+            tuple(down_w.shape) != (E, H, I):
+        raise ValueError("inconsistent shapes")
+    if tuple(workspace.shape) != (Tp, I) or tuple(out.shape) != (Tp, H):
+        raise ValueError("workspace must be [Tp, I] and out [Tp, H]")
+    if group_sizes.numel() != E or group_offsets.numel() != E + 1 or \
+            group_padded_offsets.numel() != E + 1:
+        raise ValueError("group tables must have E, E+1, E+1 entries")
+    pairs = routed_expert_weights.numel()
+    M = group_idx_for_bx.numel()
+    f16, i32 = torch.float16, torch.int32
+    st = lib().rmoe_forward_f16_variant(
+        _dev(x, f16, "stacked_expert_tokens"), _dev(gate_w, f16, "gate_w"),
+        _dev(up_w, f16, "up_w"), _dev(down_w, f16, "down_w"),
+        _dev(routed_expert_weights, torch.float32, "routed_expert_weights"),
+        _dev(group_sizes, i32, "group_sizes"), _dev(group_offsets, i32, "group_offsets"),
+        _dev(group_padded_offsets, i32, "group_padded_offsets"),
+        _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
+        _dev(out, f16, "out"), H, I, E, Tp, pairs, M, _VARIANTS[variant], _stream(x, stream))
+    _check(st, "rmoe_forward_f16")
+
+
+def gate_up(stacked_expert_tokens, gate_w, up_w, group_sizes, group_padded_offsets,
+            group_idx_for_bx, workspace, variant="auto", stream=None):
+    """Stage 1 alone: workspace = fp16(silu(x Wg^T) * (x Wu^T)) on valid rows."""
+    torch = _torch()
+    x = stacked_expert_tokens
+    E, I, H = gate_w.shape
+    f16, i32 = torch.float16, torch.int32
+    st = lib().rmoe_gate_up_f16(
+        _dev(x, f16, "stacked_expert_tokens"), _dev(gate_w, f16, "gate_w"),
+        _dev(up_w, f16, "up_w"), _dev(group_sizes, i32, "group_sizes"),
+        _dev(group_padded_offsets, i32, "group_padded_offsets"),
+        _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
+        H, I, E, x.shape[0], group_idx_for_bx.numel(), _VARIANTS[variant], _stream(x, stream))
+    _check(st, "rmoe_gate_up_f16")
+
+
+def down(workspace, down_w, routed_expert_weights, group_sizes, group_offsets,
+         group_padded_offsets, group_idx_for_bx, out, variant="auto", stream=None):
+    """Stage 2 alone: out = fp16((hidden Wd^T) * w[compact row]) on valid rows."""
+    torch = _torch()
+    E, H, I = down_w.shape
+    f16, i32 = torch.float16, torch.int32
+    st = lib().rmoe_down_f16(
+        _dev(workspace, f16, "workspace"), _dev(down_w, f16, "down_w"),
+        _dev(routed_expert_weights, torch.float32, "routed_expert_weights"),
+        _dev(group_sizes, i32, "group_sizes"), _dev(group_offsets, i32, "group_offsets"),
+        _dev(group_padded_offsets, i32, "group_padded_offsets"),
+        _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(out, f16, "out"), H, I, E,
+        workspace.shape[0], routed_expert_weights.numel(), group_idx_for_bx.numel(),
+        _VARIANTS[variant], _stream(workspace, stream))
+    _check(st, "rmoe_down_f16")
+
+
+def pack(x, topk_weights, padded_row_of_pair, compact_pos_of_pair, stacked, w_compact,
+         stream=None):
+    """Gather token rows into the padded expert-sorted layout and the routed
+    weights into compact order (device tensors)."""
+    torch = _torch()
+    T, H = x.shape
+    pairs = topk_weights.numel()
+    k = pairs // T if T else 0
+    st = lib().rmoe_pack_f16(
+        _dev(x, torch.float16, "x"), _dev(topk_weights, torch.float32, "topk_weights"),
+        _dev(padded_row_of_pair, torch.int32, "padded_row_of_pair"),
+        _dev(compact_pos_of_pair, torch.int32, "compact_pos_of_pair"), T, k, H,
+        _dev(stacked, torch.float16, "stacked"), _dev(w_compact, torch.float32, "w_compact"),
+        stacked.shape[0], _stream(x, stream))
+    _check(st, "rmoe_pack_f16")
+
+
+def combine(out, padded_row_of_pair, top_k, y, stream=None):
+    """y[t] = fp16(sum over the token's k slots of out[padded row])."""
+    torch = _torch()
+    T, H = y.shape
+    st = lib().rmoe_combine_f16(
+        _dev(out, torch.float16, "out"), _dev(padded_row_of_pair, torch.int32, "padded_row_of_pair"),
+        T, int(top_k), H, _dev(y, torch.float16, "y"), out.shape[0], _stream(out, stream))
+    _check(st, "rmoe_combine_f16")
+
+
+_WORKSPACE = {}
+
+
+def _get_workspace(stacked_expert_tokens, intermediate):
+    torch = _torch()
+    x = stacked_expert_tokens
+    key = (x.device.index or 0, int(x.shape[0]), int(intermediate), str(x.dtype))
+    ws = _WORKSPACE.get(key)
+    if ws is None:
+        ws = torch.empty((int(x.shape[0]), int(intermediate)), device=x.device, dtype=x.dtype)
+        _WORKSPACE[key] = ws
+    return ws
+
+
+def run_kernel(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
+               group_offsets, group_padded_offsets, group_idx_for_bx, out):
+    """Submission-style entry: derives the sizes from the tensors, uses a
+    cached workspace, enqueues the forward; no sync, no return value."""
+    ws = _get_workspace(stacked_expert_tokens, gate_w.shape[1])
+    forward(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
+            group_offsets, group_padded_offsets, group_idx_for_bx, ws, out)

@@ -1,0 +1,303 @@
+// C-ABI entry points of the routed fused-MoE library: host-side dispatch
+// contract, its validator, argument checking and kernel dispatch.  Nothing
+// here allocates device memory, synchronises, or reads device tables.
+#include "../../include/routed_moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "rmoe_internal.h"
+
+namespace {
+
+constexpr int64_t B = RMOE_BLOCK_M;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks shared by the forward and the two stage entry points.
+int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
+               int64_t total_padded_tokens, int32_t num_blocks_m) {
+    if (hidden <= 0 || intermediate <= 0 || num_experts < 1 || num_blocks_m < 0 ||
+        total_padded_tokens < 0)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (hidden % 128 != 0 || intermediate % 128 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    if ((int64_t)num_blocks_m * B > total_padded_tokens) return RMOE_ERR_INVALID_ARGUMENT;
+    if (num_blocks_m > 65535) return RMOE_ERR_UNSUPPORTED_SHAPE;  // grid y limit
+    if (hidden > (int64_t)1 << 20 || intermediate > (int64_t)1 << 20)
+        return RMOE_ERR_UNSUPPORTED_SHAPE;
+    return RMOE_OK;
+}
+
+// Kernel family: the weight-streaming family when blocks hold few rows on
+// average (then a weight byte serves at most a handful of tokens and the
+// stage is HBM-bound), the LDS-tiled family otherwise.
+int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts) {
+    if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
+    return pairs <= 48 * (int64_t)num_experts ? RMOE_VARIANT_STREAM : RMOE_VARIANT_TILE;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? RMOE_OK : RMOE_ERR_LAUNCH; }
+
+int gate_up_impl(const void *x, const void *gate_w, const void *up_w, const int32_t *gs,
+                 const int32_t *gpo, const int32_t *gidx, void *workspace, int64_t hidden,
+                 int64_t intermediate, int32_t E, int64_t Tp, int32_t M, int64_t pairs,
+                 int32_t variant, void *stream) {
+    rmoe::StageArgs a{};
+    a.x = static_cast<const _Float16 *>(x);
+    a.w0 = static_cast<const _Float16 *>(gate_w);
+    a.w1 = static_cast<const _Float16 *>(up_w);
+    a.gs = gs;
+    a.gpo = gpo;
+    a.gidx = gidx;
+    a.y = static_cast<_Float16 *>(workspace);
+    a.K = hidden;
+    a.N = intermediate;
+    a.E = E;
+    a.M = M;
+    a.pairs = pairs;
+    (void)Tp;
+    if (M == 0) return RMOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
+        return to_status(rmoe::launch_stream_gate_up(a, s));
+    return to_status(rmoe::launch_tile_gate_up(a, s));
+}
+
+int down_impl(const void *workspace, const void *down_w, const float *rw, const int32_t *gs,
+              const int32_t *go, const int32_t *gpo, const int32_t *gidx, void *out,
+              int64_t hidden, int64_t intermediate, int32_t E, int64_t Tp, int32_t M,
+              int64_t pairs, int32_t variant, void *stream) {
+    rmoe::StageArgs a{};
+    a.x = static_cast<const _Float16 *>(workspace);
+    a.w0 = static_cast<const _Float16 *>(down_w);
+    a.rw = rw;
+    a.gs = gs;
+    a.go = go;
+    a.gpo = gpo;
+    a.gidx = gidx;
+    a.y = static_cast<_Float16 *>(out);
+    a.K = intermediate;
+    a.N = hidden;
+    a.E = E;
+    a.M = M;
+    a.pairs = pairs;
+    (void)Tp;
+    if (M == 0) return RMOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
+        return to_status(rmoe::launch_stream_down(a, s));
+    return to_status(rmoe::launch_tile_down(a, s));
+}
+
+bool bad_variant(int32_t v) {
+    return v != RMOE_VARIANT_AUTO && v != RMOE_VARIANT_STREAM && v != RMOE_VARIANT_TILE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rmoe_status_str(int status) {
+    switch (status) {
+        case RMOE_OK: return "ok";
+        case RMOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case RMOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case RMOE_ERR_MISALIGNED: return "misaligned pointer";
+        case RMOE_ERR_LAUNCH: return "kernel launch failed";
+        case RMOE_ERR_CONTRACT: return "tables violate the dispatch contract";
+        case RMOE_ERR_CAPACITY: return "output table too small";
+        default: return "unknown status";
+    }
+}
+
+const char *rmoe_version(void) { return "routed_moe 0.1 gfx950"; }
+
+int rmoe_build_contract(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                        int32_t num_experts, int32_t *group_sizes, int32_t *group_offsets,
+                        int32_t *group_padded_offsets, int32_t *group_idx_for_bx,
+                        int64_t capacity_blocks, int32_t *num_blocks_m, int32_t *order,
+                        int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair) {
+    if (num_tokens < 0 || top_k < 0 || num_experts < 1 || !group_sizes || !group_offsets ||
+        !group_padded_offsets || !num_blocks_m || (num_tokens > 0 && top_k > 0 && !topk_ids))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    const int64_t pairs = num_tokens * top_k;
+    if (pairs > INT32_MAX / 2) return RMOE_ERR_INVALID_ARGUMENT;
+    const int32_t E = num_experts;
+    // counts (and id range check before anything is written)
+    std::vector<int64_t> cnt(E, 0);
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int32_t e = topk_ids[p];
+        if (e < 0 || e >= E) return RMOE_ERR_INVALID_ARGUMENT;
+        cnt[e]++;
+    }
+    const int64_t M = ceil_div(pairs, B) + E;
+    if (M > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
+    if (capacity_blocks < M || (M > 0 && !group_idx_for_bx)) return RMOE_ERR_CAPACITY;
+    // compact and padded offsets (E+1 entries each)
+    group_offsets[0] = 0;
+    group_padded_offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        group_sizes[e] = (int32_t)cnt[e];
+        group_offsets[e + 1] = group_offsets[e] + (int32_t)cnt[e];
+        group_padded_offsets[e + 1] = group_padded_offsets[e] + (int32_t)(ceil_div(cnt[e] + 1, B) * B);
+    }
+    *num_blocks_m = (int32_t)M;
+    // block -> last expert whose padded start is <= bx*128 (starts strictly increase)
+    int32_t e = 0;
+    for (int64_t bx = 0; bx < M; ++bx) {
+        while (e + 1 < E && (int64_t)group_padded_offsets[e + 1] <= bx * B) ++e;
+        group_idx_for_bx[bx] = e;
+    }
+    // stable counting sort of the pairs by expert
+    std::vector<int32_t> next(group_offsets, group_offsets + E);
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int32_t ex = topk_ids[p];
+        const int32_t c = next[ex]++;
+        const int32_t rank = c - group_offsets[ex];
+        if (order) order[c] = (int32_t)p;
+        if (padded_row_of_pair) padded_row_of_pair[p] = group_padded_offsets[ex] + rank;
+        if (compact_pos_of_pair) compact_pos_of_pair[p] = c;
+    }
+    return RMOE_OK;
+}
+
+int rmoe_validate_contract(const int32_t *gs, const int32_t *go, const int32_t *gpo,
+                           const int32_t *gidx, int32_t E, int32_t M, int64_t Tp, int64_t pairs) {
+    if (!gs || !go || !gpo || E < 1 || M < 0 || (M > 0 && !gidx)) return RMOE_ERR_INVALID_ARGUMENT;
+    if (go[0] != 0 || gpo[0] != 0) return RMOE_ERR_CONTRACT;
+    for (int32_t e = 0; e < E; ++e) {
+        if (gs[e] < 0) return RMOE_ERR_CONTRACT;
+        if ((int64_t)go[e + 1] - go[e] != gs[e]) return RMOE_ERR_CONTRACT;
+        if ((int64_t)gpo[e + 1] - gpo[e] != ((int64_t)gs[e] / B + 1) * B) return RMOE_ERR_CONTRACT;
+    }
+    if ((int64_t)go[E] != pairs) return RMOE_ERR_CONTRACT;
+    if ((int64_t)M != ceil_div(pairs, B) + E) return RMOE_ERR_CONTRACT;
+    if ((int64_t)gpo[E] > (int64_t)M * B || (int64_t)M * B > Tp) return RMOE_ERR_CONTRACT;
+    int32_t e = 0;
+    for (int64_t bx = 0; bx < M; ++bx) {
+        while (e + 1 < E && (int64_t)gpo[e + 1] <= bx * B) ++e;
+        if (gidx[bx] != e) return RMOE_ERR_CONTRACT;
+    }
+    return RMOE_OK;
+}
+
+size_t rmoe_workspace_bytes(int64_t total_padded_tokens, int64_t intermediate) {
+    if (total_padded_tokens <= 0 || intermediate <= 0) return 0;
+    return (size_t)total_padded_tokens * (size_t)intermediate * 2u;
+}
+
+int rmoe_gate_up_f16(const void *x, const void *gate_w, const void *up_w, const int32_t *gs,
+                     const int32_t *gpo, const int32_t *gidx, void *workspace, int64_t hidden,
+                     int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
+                     int32_t num_blocks_m, int32_t variant, void *stream) {
+    int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
+    if (st != RMOE_OK) return st;
+    if (bad_variant(variant)) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!x || !gate_w || !up_w || !gs || !gpo || !workspace || (num_blocks_m > 0 && !gidx))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(gate_w) || !aligned16(up_w) || !aligned16(workspace) ||
+        !aligned4(gs) || !aligned4(gpo) || !aligned4(gidx))
+        return RMOE_ERR_MISALIGNED;
+    // without the compact offsets the average group size is unknown: the
+    // variant decides, AUTO takes the tiled family only for many blocks
+    const int64_t pairs_est = ((int64_t)num_blocks_m - num_experts) * B;
+    return gate_up_impl(x, gate_w, up_w, gs, gpo, gidx, workspace, hidden, intermediate,
+                        num_experts, total_padded_tokens, num_blocks_m, pairs_est, variant,
+                        stream);
+}
+
+int rmoe_down_f16(const void *workspace, const void *down_w, const float *rw, const int32_t *gs,
+                  const int32_t *go, const int32_t *gpo, const int32_t *gidx, void *out,
+                  int64_t hidden, int64_t intermediate, int32_t num_experts,
+                  int64_t total_padded_tokens, int64_t total_valid_tokens, int32_t num_blocks_m,
+                  int32_t variant, void *stream) {
+    int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
+    if (st != RMOE_OK) return st;
+    if (bad_variant(variant) || total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!workspace || !down_w || !gs || !go || !gpo || !out || (num_blocks_m > 0 && !gidx) ||
+        (total_valid_tokens > 0 && !rw))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(workspace) || !aligned16(down_w) || !aligned16(out) || !aligned4(rw) ||
+        !aligned4(gs) || !aligned4(go) || !aligned4(gpo) || !aligned4(gidx))
+        return RMOE_ERR_MISALIGNED;
+    return down_impl(workspace, down_w, rw, gs, go, gpo, gidx, out, hidden, intermediate,
+                     num_experts, total_padded_tokens, num_blocks_m, total_valid_tokens, variant,
+                     stream);
+}
+
+int rmoe_forward_f16_variant(const void *x, const void *gate_w, const void *up_w,
+                             const void *down_w, const float *rw, const int32_t *gs,
+                             const int32_t *go, const int32_t *gpo, const int32_t *gidx,
+                             void *workspace, void *out, int64_t hidden, int64_t intermediate,
+                             int32_t num_experts, int64_t total_padded_tokens,
+                             int64_t total_valid_tokens, int32_t num_blocks_m, int32_t variant,
+                             void *stream) {
+    int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
+    if (st != RMOE_OK) return st;
+    if (bad_variant(variant) || total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!x || !gate_w || !up_w || !down_w || !gs || !go || !gpo || !workspace || !out ||
+        (num_blocks_m > 0 && !gidx) || (total_valid_tokens > 0 && !rw))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(gate_w) || !aligned16(up_w) || !aligned16(down_w) ||
+        !aligned16(workspace) || !aligned16(out) || !aligned4(rw) || !aligned4(gs) ||
+        !aligned4(go) || !aligned4(gpo) || !aligned4(gidx))
+        return RMOE_ERR_MISALIGNED;
+    const int v = pick_variant(variant, total_valid_tokens, num_experts);
+    st = gate_up_impl(x, gate_w, up_w, gs, gpo, gidx, workspace, hidden, intermediate,
+                      num_experts, total_padded_tokens, num_blocks_m, total_valid_tokens, v,
+                      stream);
+    if (st != RMOE_OK) return st;
+    return down_impl(workspace, down_w, rw, gs, go, gpo, gidx, out, hidden, intermediate,
+                     num_experts, total_padded_tokens, num_blocks_m, total_valid_tokens, v,
+                     stream);
+}
+
+int rmoe_forward_f16(const void *x, const void *gate_w, const void *up_w, const void *down_w,
+                     const float *rw, const int32_t *gs, const int32_t *go, const int32_t *gpo,
+                     const int32_t *gidx, void *workspace, void *out, int64_t hidden,
+                     int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
+                     int64_t total_valid_tokens, int32_t num_blocks_m, void *stream) {
+    return rmoe_forward_f16_variant(x, gate_w, up_w, down_w, rw, gs, go, gpo, gidx, workspace,
+                                    out, hidden, intermediate, num_experts, total_padded_tokens,
+                                    total_valid_tokens, num_blocks_m, RMOE_VARIANT_AUTO, stream);
+}
+
+int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,
+                  const int32_t *cpos, int64_t num_tokens, int32_t top_k, int64_t hidden,
+                  void *stacked, float *w_compact, int64_t total_padded_tokens, void *stream) {
+    if (num_tokens < 0 || top_k < 0 || hidden <= 0 || total_padded_tokens < 0)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (hidden % 8 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    const int64_t pairs = num_tokens * top_k;
+    if (pairs == 0) return RMOE_OK;
+    if (!x || !topk_weights || !prow || !cpos || !stacked || !w_compact)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(stacked) || !aligned4(topk_weights) || !aligned4(prow) ||
+        !aligned4(cpos) || !aligned4(w_compact))
+        return RMOE_ERR_MISALIGNED;
+    (void)total_padded_tokens;
+    return to_status(rmoe::launch_pack(static_cast<const _Float16 *>(x), topk_weights, prow, cpos,
+                                       pairs, top_k, hidden, static_cast<_Float16 *>(stacked),
+                                       w_compact, static_cast<hipStream_t>(stream)));
+}
+
+int rmoe_combine_f16(const void *out, const int32_t *prow, int64_t num_tokens, int32_t top_k,
+                     int64_t hidden, void *y, int64_t total_padded_tokens, void *stream) {
+    if (num_tokens < 0 || top_k < 0 || hidden <= 0 || total_padded_tokens < 0)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (hidden % 8 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    if (num_tokens == 0) return RMOE_OK;
+    if (!y || (top_k > 0 && (!out || !prow))) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(y) || !aligned16(out) || !aligned4(prow)) return RMOE_ERR_MISALIGNED;
+    (void)total_padded_tokens;
+    return to_status(rmoe::launch_combine(static_cast<const _Float16 *>(out), prow, num_tokens,
+                                          top_k, hidden, static_cast<_Float16 *>(y),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the
+// block -> (expert, rows) predicate and the SwiGLU gate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmoe {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
+
+constexpr int kBlockM = 128;  // rows per contract block (block_token)
+
+// Expert and valid-row count of block bx: the row predicate shared by the
+// Step-1 and Step-2 grids ("Fused MoE GEMM 提交说明", 完整算子代码):
+// actual_rows = max(0, min(128, group_size - (bx*128 - padded_start))).
+struct BlockInfo {
+    int e;             // expert of the block
+    int token_offset;  // bx*128 - group_padded_offsets[e]
+    int rows;          // valid rows in [0, 128]
+};
+
+__device__ __forceinline__ BlockInfo block_info(const int32_t *__restrict__ gs,
+                                                const int32_t *__restrict__ gpo,
+                                                const int32_t *__restrict__ gidx, int bx) {
+    BlockInfo b;
+    b.e = gidx[bx];
+    b.token_offset = bx * kBlockM - gpo[b.e];
+    int r = gs[b.e] - b.token_offset;
+    b.rows = r < 0 ? 0 : (r > kBlockM ? kBlockM : r);
+    return b;
+}
+
+// silu(g) = g * sigmoid(g) = g / (1 + e^-g), with the hardware exp2.
+__device__ __forceinline__ float silu(float g) {
+    return g / (1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
+
+__device__ __forceinline__ h4 to_h4(float a, float b, float c, float d) {
+    h4 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    r[2] = (_Float16)c;
+    r[3] = (_Float16)d;
+    return r;
+}
+
+}  // namespace rmoe

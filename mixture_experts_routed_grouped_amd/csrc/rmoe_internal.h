@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI host code (rmoe_api.cpp) and the
+// gfx950 kernel launchers (*.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmoe {
+
+// One stage of the routed expert FFN as the kernels see it: a grouped GEMM
+// Y[r, n] = epilogue( sum_k X[r, k] * W[e(r), n, k] ) over the valid rows r
+// of every 128-row block.  For the gate/up stage W0 = gate_w, W1 = up_w and
+// the epilogue is fp16(silu(g) * u); for the down stage W0 = down_w and the
+// epilogue is fp16(acc * routed_weight[compact row]).
+struct StageArgs {
+    const _Float16 *x;      // [Tp, K]
+    const _Float16 *w0;     // [E, N, K]
+    const _Float16 *w1;     // [E, N, K] (gate/up only)
+    const float *rw;        // [pairs] compact order (down only)
+    const int32_t *gs;      // group_sizes [E]
+    const int32_t *go;      // group_offsets [E+1] (down only)
+    const int32_t *gpo;     // group_padded_offsets [E+1]
+    const int32_t *gidx;    // group_idx_for_bx [M]
+    _Float16 *y;            // [Tp, N]
+    int64_t K, N;
+    int32_t E, M;
+    int64_t pairs;
+};
+
+// Kernel-family launchers; return hipSuccess or the launch error.
+hipError_t launch_stream_gate_up(const StageArgs &a, hipStream_t s);
+hipError_t launch_stream_down(const StageArgs &a, hipStream_t s);
+hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s);
+hipError_t launch_tile_down(const StageArgs &a, hipStream_t s);
+
+hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,
+                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H,
+                       _Float16 *stacked, float *w_compact, hipStream_t s);
+hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, int32_t top_k,
+                          int64_t H, _Float16 *y, hipStream_t s);
+
+}  // namespace rmoe

@@ -1,0 +1,80 @@
+// Token packing and combine around the routed kernel: pure data movement,
+// bound by HBM.  Each thread moves 16-byte chunks (8 fp16), consecutive
+// threads take consecutive chunks of one row, so every row is read and
+// written with full coalesced lines.
+#include "rmoe_device.h"
+#include "rmoe_internal.h"
+
+namespace rmoe {
+namespace {
+
+// stacked[prow[p]] = x[p / k]; w_compact[cpos[p]] = topk_w[p]
+__global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ x,
+                                                   const float *__restrict__ topk_w,
+                                                   const int32_t *__restrict__ prow,
+                                                   const int32_t *__restrict__ cpos, int64_t pairs,
+                                                   int32_t k, int64_t chunks_per_row,
+                                                   _Float16 *__restrict__ stacked,
+                                                   float *__restrict__ w_compact) {
+    const int64_t total = pairs * chunks_per_row;
+    const int64_t H = chunks_per_row * 8;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = i / chunks_per_row, c = i - p * chunks_per_row;
+        const int64_t t = p / k;
+        *(h8 *)(stacked + (int64_t)prow[p] * H + 8 * c) = *(const h8 *)(x + t * H + 8 * c);
+        if (c == 0) w_compact[cpos[p]] = topk_w[p];
+    }
+}
+
+// y[t] = fp16(sum_j out[prow[t*k + j]]), fp32 sum in slot order
+__global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict__ out,
+                                                      const int32_t *__restrict__ prow, int64_t T,
+                                                      int32_t k, int64_t chunks_per_row,
+                                                      _Float16 *__restrict__ y) {
+    const int64_t total = T * chunks_per_row;
+    const int64_t H = chunks_per_row * 8;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / chunks_per_row, c = i - t * chunks_per_row;
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            const h8 v = *(const h8 *)(out + (int64_t)prow[t * k + j] * H + 8 * c);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s[q] += (float)v[q];
+        }
+        h8 r;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r[q] = (_Float16)s[q];
+        *(h8 *)(y + t * H + 8 * c) = r;
+    }
+}
+
+unsigned grid_for(int64_t total) {
+    int64_t g = (total + 255) / 256;
+    if (g > 256 * 64) g = 256 * 64;  // grid-stride beyond 64 workgroups per CU
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,
+                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H,
+                       _Float16 *stacked, float *w_compact, hipStream_t s) {
+    if (pairs == 0) return hipSuccess;
+    const int64_t cpr = H / 8;
+    hipLaunchKernelGGL(pack_kernel, dim3(grid_for(pairs * cpr)), dim3(256), 0, s, x, topk_w, prow,
+                       cpos, pairs, top_k, cpr, stacked, w_compact);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, int32_t top_k,
+                          int64_t H, _Float16 *y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int64_t cpr = H / 8;
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * cpr)), dim3(256), 0, s, out, prow, T,
+                       top_k, cpr, y);
+    return hipGetLastError();
+}
+
+}  // namespace rmoe

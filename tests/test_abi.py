@@ -1,0 +1,132 @@
+"""CPU-side tests of the C-ABI library: it loads, exports every symbol the
+header declares, its C++ contract builder matches the contract oracle bit
+for bit, its validator accepts valid tables and rejects corrupted ones, and
+bad arguments return the documented status without touching the GPU."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mixture_experts_routed_grouped_amd as R
+import workloads
+from oracle import contract as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "routed_moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"RMOE_API\s+[\w\s\*]+?\b(rmoe_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 11
+    L = ctypes.CDLL(R.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(R._SIGS), "binding and header disagree"
+
+
+def _compare_tables(lib_c, orc):
+    for key in ["group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx",
+                "order", "padded_row_of_pair", "compact_pos_of_pair"]:
+        assert np.asarray(lib_c[key]).tolist() == list(orc[key]), key
+    assert lib_c["num_blocks_m"] == orc["num_blocks_m"]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_contract_matches_oracle_random(seed):
+    rng = np.random.default_rng(500 + seed)
+    E = int(rng.integers(1, 40))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.integers(0, 1500))
+    cfg = workloads.Config("r", T, E, k, 128, 128, routing="zipf" if seed % 2 else "uniform",
+                           zipf_s=1.2, seed=seed)
+    ids = workloads.draw_routing(cfg)
+    _compare_tables(R.build_contract(ids, E), C.build_contract(ids.tolist(), E))
+
+
+def test_contract_matches_oracle_workloads():
+    for name, cfg in workloads.CONFIGS.items():
+        ids = workloads.draw_routing(cfg)
+        _compare_tables(R.build_contract(ids, cfg.experts), C.build_contract(ids.tolist(), cfg.experts))
+
+
+def test_contract_handworked():
+    with open(os.path.join(ROOT, "tests", "golden", "contract_handworked.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        ids = workloads.routing_from_counts(case["counts"], seed=1)
+        c = R.build_contract(ids, case["experts"])
+        for key in ["group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx"]:
+            assert c[key].tolist() == case[key]
+        assert c["num_blocks_m"] == case["num_blocks_m"]
+
+
+def test_validate_contract():
+    ids = workloads.draw_routing(workloads.CONFIGS["fine"])
+    c = R.build_contract(ids, 64)
+    args = [c["group_sizes"], c["group_offsets"], c["group_padded_offsets"], c["group_idx_for_bx"]]
+    tail = (64, c["num_blocks_m"], c["total_padded_tokens"], c["pairs"])
+    assert R.validate_contract(*args, *tail) == 0
+    bad = [a.copy() for a in args]
+    bad[3][5] += 1                                        # a block mapped to the wrong expert
+    assert R.validate_contract(*bad, *tail) == -5
+    bad = [a.copy() for a in args]
+    bad[2][3:] += 128                                     # padded span without the slack rule
+    assert R.validate_contract(*bad, *tail) == -5
+    bad = [a.copy() for a in args]
+    bad[1][7] -= 1                                        # offsets inconsistent with sizes
+    assert R.validate_contract(*bad, *tail) == -5
+    assert R.validate_contract(*args, 64, c["num_blocks_m"], c["total_padded_tokens"] - 128,
+                               c["pairs"]) == -5          # padded buffer too short
+    assert R.validate_contract(*args, 64, c["num_blocks_m"], c["total_padded_tokens"],
+                               c["pairs"] + 1) == -5
+
+
+def test_build_contract_errors():
+    L = R.lib()
+    ids = np.array([[0, 4]], np.int32)                    # id out of range
+    with pytest.raises(R.RmoeError):
+        R.build_contract(ids, 4)
+    gs = np.zeros(4, np.int32)
+    go = np.zeros(5, np.int32)
+    gpo = np.zeros(5, np.int32)
+    gidx = np.zeros(1, np.int32)
+    M = np.zeros(1, np.int32)
+    ids = np.zeros((300, 1), np.int32)
+    p = lambda a: ctypes.c_void_p(a.ctypes.data)
+    st = L.rmoe_build_contract(p(ids), 300, 1, 4, p(gs), p(go), p(gpo), p(gidx), 1, p(M), None,
+                               None, None)
+    assert st == -6                                       # capacity too small
+
+
+def test_argument_errors_without_gpu():
+    """Argument checks run before any HIP call, so they are testable here."""
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)       # aligned non-null stand-in; never dereferenced
+    odd = ctypes.c_void_p(0x10002)
+    ptrs = [fake] * 11
+
+    def fwd(p, H=256, I=128, E=4, Tp=640, pairs=18, M=5, variant=0):
+        return L.rmoe_forward_f16_variant(*p, H, I, E, Tp, pairs, M, variant, None)
+
+    assert fwd([None] + ptrs[1:]) == -1                   # null tokens
+    assert fwd(ptrs, H=200) == -2                         # hidden not a multiple of 128
+    assert fwd(ptrs, I=96) == -2
+    assert fwd(ptrs, E=0) == -1
+    assert fwd(ptrs, Tp=512) == -1                        # num_blocks_m*128 > Tp
+    assert fwd(ptrs, pairs=-1) == -1
+    assert fwd(ptrs, variant=7) == -1
+    assert fwd([odd] + ptrs[1:]) == -3                    # misaligned fp16 tensor
+    assert L.rmoe_gate_up_f16(*([fake] * 7), 256, 100, 4, 640, 5, 0, None) == -2
+    assert L.rmoe_down_f16(*([fake] * 8), 256, 128, 4, 640, -3, 5, 0, None) == -1
+    assert L.rmoe_pack_f16(fake, fake, fake, fake, 3, 2, 12, fake, fake, 640, None) == -2
+    assert L.rmoe_combine_f16(fake, fake, -1, 2, 16, fake, 640, None) == -1
+    assert L.rmoe_workspace_bytes(640, 128) == 640 * 128 * 2
+    assert R.status_str(-5).startswith("tables violate")
