@@ -3,9 +3,17 @@
 Bar (the target's stated tolerance): every valid element of out satisfies
 |gpu - oracle| <= 2e-2 + 2e-2 |oracle|; the contract tables match bit for
 bit; padding rows of out and of the workspace are never written.  Tighter
-diagnostics ride along: the fp16 hidden workspace within 2 fp16 ulps (the
-fp32 summation order differs), and the relative RMS error of out below
-2e-3 (a dropped K tile would show as ~1e-1)."""
+diagnostics ride along: the fp16 hidden workspace within 2 fp16 ulps plus an
+absolute 3e-5, with at most 1% of entries more than 1 ulp apart, and the
+relative RMS error of out below 2e-3 (a dropped K tile would show as ~1e-1).
+
+Why the absolute term: gate and up are fp32 sums of K = H products whose
+magnitudes add up to ~40 at the workload sizes, so either side's summation
+order leaves an absolute error of order 2^-24 * sqrt(K) * 40 ~ 1e-6..1e-5.
+Where gate or up nearly cancels, the fp16 hidden is tiny and that absolute
+error spans many of its ulps.  Measured against float64 on the decode
+workload, the MFMA path was the closer of the two (worst 5.5 ulps vs 18.4
+ulps for the oracle's sequential fp32 sum, mean 0.25 ulp for both)."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +43,10 @@ def _assert_parity(gpu_hid, gpu_out, o_hid, o_out, what):
     bad = d > ATOL + RTOL * np.abs(oo)
     assert not bad.any(), f"{what}: {bad.sum()} out elements beyond tolerance, max {d.max()}"
     dh = np.abs(gh - oh)
-    assert np.all(dh <= 2 * ulp16(np.maximum(np.abs(gh), np.abs(oh))) + 2.0 ** -20), \
-        f"{what}: hidden beyond 2 ulps, max {dh.max()}"
+    u = ulp16(np.maximum(np.abs(gh), np.abs(oh)))
+    over = dh > 2 * u + 3e-5
+    assert not over.any(), f"{what}: {over.sum()} hidden entries beyond 2 ulps + 3e-5, max {dh.max()}"
+    assert np.count_nonzero(dh > u) <= 0.01 * dh.size, f"{what}: too many hidden entries > 1 ulp"
     rel = np.sqrt((d ** 2).sum() / max((oo ** 2).sum(), 1e-30))
     assert rel < 2e-3, f"{what}: relative RMS error {rel}"
     return rel
@@ -100,7 +110,7 @@ def test_single_expert_and_no_pairs(variant):
     _full_compare(workloads.make_inputs(cfg, topk_ids=ids), variant)
 
 
-def test_determinism_and_variants_agree():
+def test_determinism():
     cfg = workloads.Config("det", 400, 6, 2, 256, 256, routing="zipf", zipf_s=1.3, seed=8)
     inp = workloads.make_inputs(cfg)
     d = prepare(inp)
