@@ -44,7 +44,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (x steps), the "
+                         "reference that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int, steps: int):
+    """A plain copy kernel of known size for counter calibration: each launch
+    reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n * 2,
+                      "bytes_written_per_launch": n * 2, "launches": steps}), flush=True)
 
 
 def kernel_src_hash(which: str) -> str:
@@ -144,6 +161,9 @@ def cpu_baseline(cfg, inp, target_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, args.steps)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this routed-kernel build has no multi-GPU path "
               "(expert/tensor sharding is a design note, not code). Run with --gpus 1.",
