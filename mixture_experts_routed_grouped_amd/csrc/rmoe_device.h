@@ -48,4 +48,35 @@ __device__ __forceinline__ h4 to_h4(float a, float b, float c, float d) {
     return r;
 }
 
+// ---- global -> LDS staging shared by the LDS-fed kernels.  An LDS row holds
+// 64 K-elements of one matrix row (one 128-byte line) as eight 16-byte chunks.
+
+// Physical 16-byte position of logical chunk c in LDS row r.  A 256-byte
+// sweep of the 64 banks holds two rows; XOR-ing the chunk with (r / 2) % 8
+// gives the 16 consecutive rows of an operand read (ds_read_b128, 16 lanes
+// per LDS cycle) distinct banks.
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ lds_swz(r)) << 4); }
+
+// One 1 KB global -> LDS DMA (global_load_lds_dwordx4): lane i stores the
+// 16 bytes at g to LDS byte lds + 16 i.  Counted by vmcnt like a load.
+__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
+// Bare workgroup barrier: no memory fence, so outstanding DMAs stay in flight.
+__device__ __forceinline__ void bar() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace rmoe

@@ -1,21 +1,26 @@
 // Weight-streaming grouped GEMM for blocks with few valid rows (decode-
-// shaped batches).  Such blocks make the expert FFN bound by reading the
-// expert weights from HBM (with few tokens per expert the padded expert
-// GEMMs turn memory-bound, as the contract tutorial notes), so this family
-// is organised around keeping many weight bytes in flight:
+// shaped batches).  With few tokens per expert the padded expert GEMMs turn
+// memory-bound (as the contract tutorial notes): the time is the time to
+// read the routed experts' weights from HBM once, so this family is built
+// around the access pattern HBM serves fastest.
 //
-//   * one workgroup = one 128-row block x TF output features (TF = 16 or
-//     32), KS waves that split K; each wave streams its contiguous K range
-//     of the TF weight rows straight from HBM into MFMA operand registers --
-//     no LDS staging, every weight byte is read once per 32-token pass;
-//   * weights are the MFMA A operand (feature rows), tokens the B operand,
-//     so a lane ends up with 4 consecutive features of one token (8-byte
-//     fp16 stores).  TF = 32 uses v_mfma_f32_32x32x16_f16 (one token
-//     fragment serves 32 features); TF = 16 uses v_mfma_f32_16x16x32_f16
-//     with two 16-token groups;
-//   * a ring of D chunk buffers in registers: the loads of chunk c+D-1 are
-//     issued before the MFMAs of chunk c; weight loads are non-temporal (each
-//     byte is used once), so the token rows stay in L2;
+//   * one workgroup = one 128-row block x 32 output features; KS waves split
+//     K into contiguous ranges and run independently until the final
+//     reduction (no barrier in the K loop);
+//   * weights travel HBM -> LDS by direct DMA (global_load_lds_dwordx4) in
+//     chunks of K = 64: each instruction reads 8 weight rows x 128 bytes.
+//     Measured on MI355X, that pattern streams from HBM at ~5.9 TB/s, while
+//     loading the MFMA operand layout straight into registers (32 rows x
+//     32 bytes per instruction) reaches ~4 TB/s.  Each wave owns a ring of
+//     D chunk slots, refilled D-1 chunks ahead; MFMA operands come back out
+//     of LDS with swizzled, conflict-free ds_read_b128;
+//   * a 32-token tile of the block rides in the same slots (tokens are
+//     shared by all workgroups of the block and come from L2), so every
+//     global read is a DMA and the only waits are the explicit vmcnt ones;
+//     blocks with more than 32 valid rows take one pass per tile;
+//   * weights are the MFMA A operand (v_mfma_f32_32x32x16_f16, 32 feature
+//     rows), tokens the B operand; a lane ends up with 4 consecutive
+//     features of one token, so stores are 8-byte fp16 quads;
 //   * the KS partial sums are added in a fixed order through LDS
 //     (deterministic, no atomics), the epilogue is split over the waves.
 //
@@ -26,272 +31,192 @@
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
-#ifndef RMOE_GU_MF
-#define RMOE_GU_MF 32
-#endif
 #ifndef RMOE_GU_KS
-#define RMOE_GU_KS 4
+#define RMOE_GU_KS 4  // waves (K ranges) per workgroup, gate/up
 #endif
 #ifndef RMOE_GU_D
-#define RMOE_GU_D 2
-#endif
-#ifndef RMOE_DN_MF
-#define RMOE_DN_MF 32
+#define RMOE_GU_D 2   // ring slots per wave, gate/up
 #endif
 #ifndef RMOE_DN_KS
 #define RMOE_DN_KS 4
 #endif
 #ifndef RMOE_DN_D
-#define RMOE_DN_D 3
-#endif
-#ifndef RMOE_STREAM_NT
-#define RMOE_STREAM_NT 0
-#endif
-#ifndef RMOE_STREAM_ILV
-#define RMOE_STREAM_ILV 1  // K split interleaved chunk by chunk across the waves
+#define RMOE_DN_D 2
 #endif
 
 namespace rmoe {
 namespace {
 
-template <int MF>
-struct Shape {
-    static constexpr int KSTEP = MF == 16 ? 32 : 16;  // K of one MFMA
-    static constexpr int CK = 4 * KSTEP;              // K per chunk (4 MFMA steps)
-    static constexpr int NG = MF == 16 ? 2 : 1;       // token fragments per 32-token pass
-    static constexpr int NQ = MF == 16 ? 2 : 4;       // 4-register output quads per matrix
-    using Acc = std::conditional_t<MF == 16, f4, f16x>;
+constexpr int MF = 32;                // output features per workgroup (MFMA rows)
+constexpr int CK = 64;                // K per chunk: one 128-byte line per weight row
+constexpr int CHUNK_B = MF * CK * 2;  // 4 KB: one matrix's chunk
+
+template <bool DUAL, int KS, int D>
+struct StreamCfg {
+    static constexpr int NM = DUAL ? 2 : 1;            // weight matrices (gate, up)
+    static constexpr int SLOT = (NM + 1) * CHUNK_B;    // weights, then 32 token rows
+    static constexpr int WAVE_LDS = D * SLOT;          // ring of one wave
+    static constexpr int RING = KS * WAVE_LDS;
+    static constexpr int RED = KS * NM * 16 * 64 * 4;  // partial sums of one tile
+    static constexpr int LDS_BYTES = RING > RED ? RING : RED;
+    static constexpr int DMA_PER_CHUNK = 4 * (NM + 1);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert((D - 1) * DMA_PER_CHUNK < 64, "vmcnt range");
 };
 
-template <bool DUAL, int MF>
-struct Frag {
-    static constexpr int NM = DUAL ? 2 : 1;
-    h8 w[NM][4];
-    h8 x[Shape<MF>::NG][4];
-};
+// One pass: the 32-token tile starting at row p0 of block bx against the 32
+// features n0.. of the block's expert, over the whole K.
+template <bool DUAL, int KS, int D>
+__device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo &bi, int bx, int p0,
+                                            int n0, unsigned char *smem, int wave, int lane) {
+    using C = StreamCfg<DUAL, KS, D>;
+    constexpr int NM = C::NM;
+    const int64_t K = a.K, N = a.N;
+    const int lr = lane & 31, lh = lane >> 5;
 
-template <bool NT>
-__device__ __forceinline__ h8 load_w(const _Float16 *p) {
-    if constexpr (NT)
-        return __builtin_nontemporal_load(reinterpret_cast<const h8 *>(p));
-    else
-        return *reinterpret_cast<const h8 *>(p);
-}
+    // contiguous K range of this wave, in chunks
+    const int nchunks = (int)(K / CK);
+    const int c_begin = (nchunks * wave) / KS;
+    const int n = (nchunks * (wave + 1)) / KS - c_begin;
 
-template <bool DUAL, int MF, bool NT>
-__device__ __forceinline__ void chunk_load(Frag<DUAL, MF> &f, const _Float16 *w0,
-                                           const _Float16 *w1, const _Float16 *x, int64_t K,
-                                           int ng, int64_t k) {
-    constexpr int KS = Shape<MF>::KSTEP;
+    // DMA sources: instruction j of matrix m (m = NM: the token tile) moves
+    // rows 8j .. 8j+7 of the chunk; lane i takes row 8j + i/8 and physical
+    // chunk i%8, i.e. logical chunk (i%8) ^ swz(row).  Token rows past the
+    // valid ones are read (they lie inside the block) but never stored.
+    const _Float16 *src[NM + 1][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) f.w[0][s] = load_w<NT>(w0 + k + KS * s);
-    if constexpr (DUAL) {
+    for (int m = 0; m <= NM; ++m)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) f.w[1][s] = load_w<NT>(w1 + k + KS * s);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) f.x[0][s] = *reinterpret_cast<const h8 *>(x + k + KS * s);
-    if constexpr (MF == 16) {
-        if (ng > 1) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                f.x[1][s] = *reinterpret_cast<const h8 *>(x + 16 * K + k + KS * s);
-        }
-    }
-}
-
-template <bool DUAL, int MF>
-__device__ __forceinline__ void chunk_mma(const Frag<DUAL, MF> &f,
-                                          typename Shape<MF>::Acc (&acc)[2][2], int ng) {
-    constexpr int NM = DUAL ? 2 : 1;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            if constexpr (MF == 16) {
-                acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.w[m][s], f.x[0][s], acc[m][0], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+            const int r = 8 * j + (lane >> 3);
+            const int c = (lane & 7) ^ lds_swz(r);
+            int64_t row;
+            const _Float16 *mat;
+            if (m == NM) {
+                mat = a.x;
+                row = (int64_t)bx * kBlockM + p0 + r;
             } else {
-                acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.w[m][s], f.x[0][s], acc[m][0], 0, 0, 0);
+                mat = m ? a.w1 : a.w0;
+                row = (int64_t)bi.e * N + n0 + r;
             }
+            src[m][j] = mat + row * K + (int64_t)c_begin * CK + 8 * c;
         }
-    }
-    if constexpr (MF == 16) {
-        if (ng > 1) {
+    const unsigned wbase = (unsigned)(uintptr_t)smem + wave * C::WAVE_LDS;
+    const unsigned char *wring = smem + wave * C::WAVE_LDS;
+    auto dma_chunk = [&](int i, int slot) {
+#pragma unroll
+        for (int m = 0; m <= NM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dma16(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
+    };
+
+    f16x acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+
+    if (n > 0) {
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j) dma_chunk(min(j, n - 1), j);
+        for (int i = 0; i < n; ++i) {
+            // refill the slot chunk i-1 used with chunk i+D-1 (clamped: the
+            // repeats land in slots no later chunk reads), then wait for
+            // chunk i, the oldest in flight
+            dma_chunk(min(i + D - 1, n - 1), (i + D - 1) % D);
+            wait_vm<(D - 1) * C::DMA_PER_CHUNK>();
+            const unsigned char *slot = wring + (i % D) * C::SLOT;
+            h8 af[NM][4], bf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int off = lds_off(lr, 2 * s + lh);
+#pragma unroll
+                for (int m = 0; m < NM; ++m) af[m][s] = *(const h8 *)(slot + m * CHUNK_B + off);
+                bf[s] = *(const h8 *)(slot + NM * CHUNK_B + off);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
-                    acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.w[m][s], f.x[1][s], acc[m][1], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m][s], bf[s], acc[m], 0, 0, 0);
         }
     }
-}
+    wait_vm<0>();  // no DMA may land in the ring once it holds partial sums
+    __syncthreads();
 
-// Register r (0..3) of output quad q: its 4 consecutive features and token.
-//   TF = 32: token lane & 31, features 8 q + 4 (lane >> 5) + r
-//   TF = 16: quad q is token group q: token 16 q + (lane & 15), features 4 (lane >> 4) + r
-template <int MF>
-__device__ __forceinline__ void quad_pos(int q, int lane, int &tok, int &feat) {
-    if constexpr (MF == 32) {
-        tok = lane & 31;
-        feat = 8 * q + 4 * (lane >> 5);
-    } else {
-        tok = 16 * q + (lane & 15);
-        feat = 4 * (lane >> 4);
+    // ---- fixed-order reduction of the KS partial sums; output quad q (4
+    //      features) belongs to wave q % KS
+    float *red = reinterpret_cast<float *>(smem);  // [KS][NM][16][64]
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave * NM + m) * 16 + r) * 64 + lane] = acc[m][r];
+    __syncthreads();
+    const int tok = p0 + lr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q % KS != wave || tok >= bi.rows) continue;
+        float v[NM][4];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float s = red[((0 * NM + m) * 16 + 4 * q + r) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < KS; ++w) s += red[((w * NM + m) * 16 + 4 * q + r) * 64 + lane];
+                v[m][r] = s;
+            }
+        // 32x32 accumulator layout: register 4q + r holds feature 8q + 4lh + r
+        const int64_t row = (int64_t)bx * kBlockM + tok;
+        _Float16 *dst = a.y + row * N + n0 + 8 * q + 4 * lh;
+        h4 o;
+        if constexpr (DUAL) {
+            o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1], silu(v[0][2]) * v[1][2],
+                      silu(v[0][3]) * v[1][3]);
+        } else {
+            const float w = a.rw[a.go[bi.e] + bi.token_offset + tok];
+            o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
+        }
+        *reinterpret_cast<h4 *>(dst) = o;
     }
+    __syncthreads();  // the next pass refills the ring that holds red[]
 }
 
-template <int MF>
-__device__ __forceinline__ float acc_get(const typename Shape<MF>::Acc (&acc)[2], int q, int r) {
-    if constexpr (MF == 32)
-        return acc[0][4 * q + r];
-    else
-        return acc[q][r];
-}
-
-// grid: (N / MF, num_blocks_m); block: 64 * KS threads.
-template <bool DUAL, int MF, int KS, int D, bool NT>
+// grid: (N / 32, num_blocks_m); block: 64 * KS threads; dynamic LDS LDS_BYTES.
+template <bool DUAL, int KS, int D>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
-    using S = Shape<MF>;
-    using Acc = typename S::Acc;
-    constexpr int NM = DUAL ? 2 : 1;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int bx = blockIdx.y;
     const BlockInfo bi = block_info(a.gs, a.gpo, a.gidx, bx);
     if (bi.rows == 0) return;
-
-    // wave-uniform by construction; readfirstlane lets the compiler keep the
-    // K range and every loop bound in scalar registers (uniform branches)
+    // wave-uniform by construction; readfirstlane keeps the K range and the
+    // loop bounds in scalar registers (uniform branches)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int lrow = MF == 16 ? (lane & 15) : (lane & 31);  // A row / B token of this lane
-    const int koff = MF == 16 ? 8 * (lane >> 4) : 8 * (lane >> 5);
-    const int64_t K = a.K, N = a.N;
     const int n0 = blockIdx.x * MF;
+    for (int p0 = 0; p0 < bi.rows; p0 += 32) stream_pass<DUAL, KS, D>(a, bi, bx, p0, n0, smem, wave, lane);
+}
 
-    // K split.  Interleaved: wave w takes chunks w, w + KS, w + 2 KS, ... so
-    // the KS waves of a workgroup read neighbouring chunks of the same weight
-    // rows at the same time -- KS * CK * 2 contiguous bytes per row in flight
-    // instead of CK * 2 (DRAM pages are opened for longer runs).  Otherwise
-    // each wave takes one contiguous quarter of K.
-    const int nchunks = (int)(K / S::CK);
-#if RMOE_STREAM_ILV
-    const int c_begin = wave;
-    const int c_step = KS;
-    const int n_mine = (nchunks - wave + KS - 1) / KS;
-#else
-    const int c_begin = (nchunks * wave) / KS;
-    const int c_step = 1;
-    const int n_mine = (nchunks * (wave + 1)) / KS - c_begin;
-#endif
-
-    const _Float16 *w0 = a.w0 + ((int64_t)bi.e * N + n0 + lrow) * K + koff;
-    const _Float16 *w1 = DUAL ? a.w1 + ((int64_t)bi.e * N + n0 + lrow) * K + koff : nullptr;
-
-    __shared__ float red[KS > 1 ? KS : 1][NM][16][64];
-
-    for (int prow0 = 0; prow0 < bi.rows; prow0 += 32) {
-        const int left = bi.rows - prow0;
-        const int ng = (MF == 16 && left > 16) ? 2 : 1;
-        const _Float16 *x = a.x + ((int64_t)bx * kBlockM + prow0 + lrow) * K + koff;
-
-        Acc acc[2][2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int g = 0; g < 2; ++g) acc[m][g] = Acc{};
-
-        // Ring of D chunks.  Prefetches are unconditional -- past the end of
-        // the range they re-read the last chunk (an L2 hit) -- so the loop
-        // body has no load under a branch and the wait counts stay exact.
-        const int n = n_mine;
-        if (n > 0) {
-            const _Float16 *w0c = w0 + (int64_t)c_begin * S::CK;
-            const _Float16 *w1c = DUAL ? w1 + (int64_t)c_begin * S::CK : nullptr;
-            const _Float16 *xc = x + (int64_t)c_begin * S::CK;
-            Frag<DUAL, MF> ring[D];
-#pragma unroll
-            for (int j = 0; j < D - 1; ++j)
-                chunk_load<DUAL, MF, NT>(ring[j], w0c, w1c, xc, K, ng,
-                                         (int64_t)min(j, n - 1) * c_step * S::CK);
-            for (int i = 0; i < n; i += D) {
-#pragma unroll
-                for (int j = 0; j < D; ++j) {
-                    const int cc = i + j;
-                    chunk_load<DUAL, MF, NT>(ring[(j + D - 1) % D], w0c, w1c, xc, K, ng,
-                                             (int64_t)min(cc + D - 1, n - 1) * c_step * S::CK);
-                    // keep the prefetch ahead of the MFMAs: without this fence
-                    // the scheduler sinks the loads below them to save
-                    // registers and the ring degenerates to depth 1
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (cc < n) chunk_mma<DUAL, MF>(ring[j], acc, ng);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-
-        // ---- fixed-order reduction of the KS partial sums; quads split over waves
-        if constexpr (KS > 1) {
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int q = 0; q < S::NQ; ++q)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) red[wave][m][4 * q + r][lane] = acc_get<MF>(acc[m], q, r);
-            __syncthreads();
-        }
-#pragma unroll
-        for (int q = 0; q < S::NQ; ++q) {
-            if (KS > 1 && q % KS != wave) continue;  // quad q belongs to wave q % KS
-            if (MF == 16 && q >= ng) continue;
-            int tok, feat;
-            quad_pos<MF>(q, lane, tok, feat);
-            tok += prow0;
-            if (tok >= bi.rows) continue;
-            float v[NM][4];
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (KS > 1) {
-                        float s = red[0][m][4 * q + r][lane];
-#pragma unroll
-                        for (int w = 1; w < KS; ++w) s += red[w][m][4 * q + r][lane];
-                        v[m][r] = s;
-                    } else {
-                        v[m][r] = acc_get<MF>(acc[m], q, r);
-                    }
-                }
-            const int64_t row = (int64_t)bx * kBlockM + tok;
-            _Float16 *dst = a.y + row * N + n0 + feat;
-            h4 o;
-            if constexpr (DUAL) {
-                o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1],
-                          silu(v[0][2]) * v[1][2], silu(v[0][3]) * v[1][3]);
-            } else {
-                const float w = a.rw[a.go[bi.e] + bi.token_offset + tok];
-                o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
-            }
-            *reinterpret_cast<h4 *>(dst) = o;
-        }
-        if constexpr (KS > 1) __syncthreads();  // red[] is reused by the next pass
-    }
+template <bool DUAL, int KS, int D>
+hipError_t launch(const StageArgs &a, hipStream_t s) {
+    using C = StreamCfg<DUAL, KS, D>;
+    hipError_t e = hipFuncSetAttribute((const void *)stream_kernel<DUAL, KS, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
+    hipLaunchKernelGGL((stream_kernel<DUAL, KS, D>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_stream_gate_up(const StageArgs &a, hipStream_t s) {
-    constexpr int MF = RMOE_GU_MF;
-    dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
-    hipLaunchKernelGGL((stream_kernel<true, MF, RMOE_GU_KS, RMOE_GU_D, RMOE_STREAM_NT != 0>), grid,
-                       dim3(64 * RMOE_GU_KS), 0, s, a);
-    return hipGetLastError();
+    return launch<true, RMOE_GU_KS, RMOE_GU_D>(a, s);
 }
 
 hipError_t launch_stream_down(const StageArgs &a, hipStream_t s) {
-    constexpr int MF = RMOE_DN_MF;
-    dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
-    hipLaunchKernelGGL((stream_kernel<false, MF, RMOE_DN_KS, RMOE_DN_D, RMOE_STREAM_NT != 0>), grid,
-                       dim3(64 * RMOE_DN_KS), 0, s, a);
-    return hipGetLastError();
+    return launch<false, RMOE_DN_KS, RMOE_DN_D>(a, s);
 }
 
 }  // namespace rmoe

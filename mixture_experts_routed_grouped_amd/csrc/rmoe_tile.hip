@@ -15,11 +15,19 @@
 //     (token, feature) for the fused silu(gate) * up epilogue; down takes
 //     256 rows of down_w.
 // Operands travel global -> LDS by direct DMA (global_load_lds_dwordx4, no
-// register staging, no ds_write), 16-byte chunks XOR-swizzled per row so
-// that MFMA operand reads (ds_read_b128) hit distinct banks, through a ring
-// of 3 LDS stages of K = 32: the DMA of step k+2 is spread over the MFMAs of
-// step k.  The waits are explicit (vmcnt) and the barrier is a bare
-// s_barrier, because a fenced barrier would drain the DMA ring every step.
+// register staging, no ds_write) in steps of K = 64: each DMA instruction
+// reads 8 rows x 128 bytes, a pattern the MI355X L2 serves at ~56 B/clk per
+// CU (1 KB-contiguous or 64-byte runs reach ~30).  16-byte chunks are
+// XOR-swizzled per row so that MFMA operand reads (ds_read_b128) hit
+// distinct banks.  The 160 KB of LDS hold five 32 KB slots -- one K step of
+// 256 rows each: three for weights and two for tokens -- so weight DMAs run
+// two steps ahead of the MFMAs and token DMAs one step.  Weights are the
+// first-touch stream from HBM; tokens are shared by the concurrently running
+// slices of a locality group and mostly hit L2.  Within a step the memory
+// instructions (the next sub-step's operand reads, the DMAs) are issued one
+// after each MFMA, so they leave the in-order wave while the matrix core is
+// busy.  The waits are explicit (vmcnt) and the barrier is a bare s_barrier,
+// because a fenced barrier would drain the DMA ring every step.
 // Waves are 2 (weight rows) x 2 (token halves); MFMA is
 // v_mfma_f32_32x32x16_f16 with weights as A (32 feature rows) and tokens as
 // B (32 token columns).  Token tiles beyond a block's valid rows are
@@ -30,46 +38,41 @@
 #include "rmoe_internal.h"
 
 #ifndef RMOE_TILE_GROUP
-#define RMOE_TILE_GROUP 4   // weight slices per locality group (see tile_item)
+#define RMOE_TILE_GROUP 8   // weight slices per locality group (see tile_item)
 #endif
 
 namespace rmoe {
 namespace {
 
-constexpr int kXcd = 8;        // MI355X: workgroups go round-robin over 8 XCDs
-constexpr int BK = 32;         // K per step
-constexpr int ROWB = 2 * BK;   // bytes per LDS row (64)
-constexpr int WROWS = 256;     // weight rows per workgroup
-constexpr int TROWS = 256;     // token rows per workgroup (two blocks)
-constexpr int STAGE = (WROWS + TROWS) * ROWB;  // 32 KB
-constexpr int NSTAGE = 3;
-constexpr int DMA_PER_WAVE = (WROWS + TROWS) / 16 / 4;  // 16-row DMA blocks per wave per step (8)
-
-// Physical 16-byte slot of logical chunk c (0..3) in LDS row r: rows are 64
-// bytes, four rows share one 256-byte sweep of the 64 banks, and XOR-ing
-// with (r >> 2) & 3 gives the 16 consecutive rows of an operand read 16
-// distinct (row mod 4, slot) bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int loff(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
-
-// One 1 KB global -> LDS DMA: lane i stores its 16 bytes at lds + 16 i.
-__device__ __forceinline__ void dma16(const void *g, unsigned lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g)
-                 : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void bar() {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+constexpr int kXcd = 8;     // MI355X: workgroups go round-robin over 8 XCDs
+constexpr int BK = 64;      // K per step
+constexpr int ROWB = 2 * BK;  // bytes per LDS row: one 128-byte line
+constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+constexpr int RPD = 64 / CPR;   // rows per 1 KB DMA instruction (8)
+constexpr int SROWS = 256;      // rows per slot: 256 weight rows or 256 tokens
+constexpr int SLOT = SROWS * ROWB;  // 32 KB
+#ifndef RMOE_TILE_WSLOTS
+#define RMOE_TILE_WSLOTS 3
+#endif
+#ifndef RMOE_TILE_TSLOTS
+#define RMOE_TILE_TSLOTS 2
+#endif
+constexpr int NWS = RMOE_TILE_WSLOTS;  // weight slots: weight DMA runs NWS-1 steps ahead
+constexpr int NTS = RMOE_TILE_TSLOTS;  // token slots: token DMA runs NTS-1 steps ahead
+static_assert(NWS >= NTS && NTS >= 2, "slot counts");
+static_assert((NWS + NTS) * SLOT <= 160 * 1024, "LDS slots exceed 160 KB");
+constexpr int LDS_BYTES = (NWS + NTS) * SLOT;
+constexpr int DMA_HALF = SROWS / RPD / 4;  // DMAs per wave per slot fill (8)
+constexpr int DMA_PER_WAVE = 2 * DMA_HALF;  // per step: token fill, then weight fill
+constexpr int SUB = BK / 16;                // MFMA sub-steps per K step
+// vmcnt a wave may leave outstanding at the top of step k: the DMAs issued
+// after the last one step k needs (token step k when NWS > NTS)
+constexpr int VM_ALLOW = NWS > NTS ? DMA_HALF + DMA_PER_WAVE * (NTS - 2) : DMA_PER_WAVE * (NTS - 2);
+#ifndef RMOE_TILE_SPREAD
+#define RMOE_TILE_SPREAD 4
+#endif
+constexpr int DMA_SPREAD = RMOE_TILE_SPREAD;  // sub-steps a step's DMAs are spread over
+constexpr int DMA_PER_SUB = (DMA_PER_WAVE + DMA_SPREAD - 1) / DMA_SPREAD;
 
 // Work item of workgroup w in an order that keeps operand sharing inside one
 // XCD's L2.  Items (weight slice nt, block bx) are listed group by group:
@@ -93,7 +96,7 @@ __device__ __forceinline__ bool tile_item(int w, int NT, int M, int &nt, int &bx
 }
 
 // grid: ceil(NT * M / 8) * 8 workgroups of 256 threads; NT = N / 128 slices
-// for gate/up and ceil(N / 256) for down.  Dynamic LDS: NSTAGE * STAGE.
+// for gate/up and ceil(N / 256) for down.  Dynamic LDS: LDS_BYTES.
 template <bool DUAL>
 __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -117,40 +120,39 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     const int lr = lane & 31, lh = lane >> 5;
     const int ww = wave & 1, wt = wave >> 1;  // weight half, token half (= block bx + wt)
 
-    // ---- DMA sources.  Wave w moves 16-row blocks j = 0..7 of a step: LDS
-    //      rows 128 w + 16 j .. +16 (rows 0..255 weights, 256..511 tokens).
-    //      Lane i fills row (i >> 2) of the block, slot i & 3, with logical
-    //      chunk (i & 3) ^ swz(row).
+    // ---- DMA sources.  Wave w fills rows 64 w .. 64 w + 63 of every slot,
+    //      RPD rows per instruction j: lane i takes row 64 w + RPD j + i / 8,
+    //      physical chunk i % 8, i.e. logical chunk (i % 8) ^ swz(row).
     const unsigned sbase = (unsigned)(uintptr_t)smem;
     const int64_t n0 = DUAL ? (int64_t)nt * 128 : (int64_t)nt * 256;  // first output feature
-    const _Float16 *src[DMA_PER_WAVE];
+    const _Float16 *wsrc[DMA_HALF], *tsrc[DMA_HALF];
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const int r = 128 * wave + 16 * j + (lane >> 2);  // LDS row
-        const int c = (lane & 3) ^ swz(r);
-        if (r < WROWS) {
-            int64_t row;
-            const _Float16 *mat;
-            if constexpr (DUAL) {
-                mat = r < 128 ? a.w0 : a.w1;  // rows 0..127 gate, 128..255 up
-                row = n0 + (r & 127);
-            } else {
-                mat = a.w0;
-                row = n0 + r;
-            }
-            row = row < N ? row : N - 1;  // a narrow last slice: idle rows read a valid row
-            src[j] = mat + ((int64_t)b0.e * N + row) * K + 8 * c;
+    for (int j = 0; j < DMA_HALF; ++j) {
+        const int r = 64 * wave + RPD * j + lane / CPR;  // row within the slot
+        const int c = (lane % CPR) ^ lds_swz(r);
+        int64_t row;
+        const _Float16 *mat;
+        if constexpr (DUAL) {
+            mat = r < 128 ? a.w0 : a.w1;  // weight rows 0..127 gate, 128..255 up
+            row = n0 + (r & 127);
         } else {
-            const int t = r - WROWS;  // token row of the pair
-            int64_t row = (int64_t)bx * kBlockM + t;
-            if (t >= kBlockM && !has1) row -= kBlockM;  // absent second block: stay in bounds
-            src[j] = a.x + row * K + 8 * c;
+            mat = a.w0;
+            row = n0 + r;
         }
+        row = row < N ? row : N - 1;  // a narrow last slice: idle rows read a valid row
+        wsrc[j] = mat + ((int64_t)b0.e * N + row) * K + 8 * c;
+        int64_t trow = (int64_t)bx * kBlockM + r;  // token row r of the pair
+        if (r >= kBlockM && !has1) trow -= kBlockM;  // absent second block: stay in bounds
+        tsrc[j] = a.x + trow * K + 8 * c;
     }
-    auto dma_step = [&](int stage, int kt, int j0, int j1) {
-        const unsigned st = sbase + stage * STAGE + (128 * wave) * ROWB;
-#pragma unroll
-        for (int j = j0; j < j1; ++j) dma16(src[j] + (int64_t)kt * BK, st + 16 * j * ROWB);
+    const unsigned dwave = sbase + 64 * wave * ROWB;
+    // DMA d of a step: d < DMA_HALF fills the token slot, the rest the weight slot
+    auto dma_one = [&](int d, int kt_t, int kt_w, int slot_t, int slot_w) {
+        if (d < DMA_HALF)
+            dma16(tsrc[d] + (int64_t)kt_t * BK, dwave + (NWS + slot_t) * SLOT + RPD * d * ROWB);
+        else
+            dma16(wsrc[d - DMA_HALF] + (int64_t)kt_w * BK,
+                  dwave + slot_w * SLOT + RPD * (d - DMA_HALF) * ROWB);
     };
 
     // ---- MFMA operands of this wave: weight tiles t (32 rows each), token
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
         else
             wrow[t] = 128 * ww + 32 * t;
     }
-    const int trow0 = WROWS + 128 * wt;
+    const int trow0 = 128 * wt;
     const int myrows = wt ? rows1 : rows0;
     const bool wlive = DUAL || n0 + 128 * ww < N;
     const int ntt = wlive ? (myrows + 31) / 32 : 0;  // live token tiles (uniform)
@@ -178,46 +180,82 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
 
     const int nk = (int)(K / BK);
 
+    // One MFMA sub-step is 4 x NTT MFMAs (K = 16).  The memory instructions
+    // of a sub-step -- the LDS operand reads of the next sub-step and this
+    // sub-step's share of the DMA -- are issued one after each MFMA, so they
+    // leave the wave while the matrix core is busy instead of stalling it in
+    // a burst (a wave issues in order).
     auto kloop = [&](auto ntt_c) {
         constexpr int NTT = decltype(ntt_c)::value;
+        constexpr int NMF = 4 * NTT;  // MFMAs per sub-step
+        constexpr int NRD = 4 + NTT;  // operand reads per sub-step
         h8 af[2][4], bf[2][4];
-        auto read_frags = [&](const unsigned char *base, int s, int slot) {
+        auto read_one = [&](const unsigned char *wb, const unsigned char *tb, int s, int slot, int i) {
             const int ch = 2 * s + lh;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) af[slot][t] = *(const h8 *)(base + loff(wrow[t] + lr, ch));
-#pragma unroll
-            for (int u = 0; u < NTT; ++u)
-                bf[slot][u] = *(const h8 *)(base + loff(trow0 + 32 * u + lr, ch));
+            if (i < 4)
+                af[slot][i] = *(const h8 *)(wb + lds_off(wrow[i] + lr, ch));
+            else
+                bf[slot][i - 4] = *(const h8 *)(tb + lds_off(trow0 + 32 * (i - 4) + lr, ch));
         };
-        // prologue: steps 0 and 1 in flight
-        dma_step(0, 0, 0, DMA_PER_WAVE);
-        dma_step(1, min(1, nk - 1), 0, DMA_PER_WAVE);
+        // prologue: the fills that steps -(NWS-1) .. -1 would issue, in
+        // the same order (tokens of step j + NTS-1, then weights of j + NWS-1)
+#pragma unroll
+        for (int j = -(NWS - 1); j < 0; ++j) {
+            const int tt = j + NTS - 1, tw = j + NWS - 1;
+            if (tt >= 0) {
+#pragma unroll
+                for (int d = 0; d < DMA_HALF; ++d) dma_one(d, min(tt, nk - 1), 0, tt % NTS, 0);
+            }
+#pragma unroll
+            for (int d = DMA_HALF; d < DMA_PER_WAVE; ++d) dma_one(d, 0, min(tw, nk - 1), 0, tw % NWS);
+        }
         for (int kt = 0; kt < nk; ++kt) {
-            // step kt's DMAs are the oldest outstanding: allow step kt+1's
-            wait_vm<DMA_PER_WAVE>();
-            bar();  // all waves' DMAs of step kt landed; reads of step kt-1 done
-            const unsigned char *base = smem + (kt % NSTAGE) * STAGE;
-            const int nstage = (kt + 2) % NSTAGE;
-            const int kn = min(kt + 2, nk - 1);  // clamped: the ring keeps a fixed DMA count
-            if constexpr (NTT > 0) read_frags(base, 0, 0);
+            // tokens and weights of step kt landed (own DMAs), then all waves'
+            wait_vm<VM_ALLOW>();
+            bar();  // also: every wave finished reading step kt-1's slots
+            const unsigned char *wb = smem + (kt % NWS) * SLOT;
+            const unsigned char *tb = smem + (NWS + kt % NTS) * SLOT;
+            // this step's fills: clamped at the end so every step issues the
+            // same count (a repeat lands in a slot no later step reads)
+            const int kt_t = min(kt + NTS - 1, nk - 1), kt_w = min(kt + NWS - 1, nk - 1);
+            const int slot_t = (kt + NTS - 1) % NTS, slot_w = (kt + NWS - 1) % NWS;
 #pragma unroll
-            for (int s = 0; s < BK / 16; ++s) {
-                if constexpr (NTT > 0) {
-                    if (s + 1 < BK / 16) read_frags(base, s + 1, (s + 1) & 1);
+            for (int i = 0; i < NRD; ++i)
+                if (NTT > 0) read_one(wb, tb, 0, 0, i);
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                const int nrd = (NTT > 0 && s + 1 < SUB) ? NRD : 0;
+                const int ndma = s < DMA_SPREAD ? min(DMA_PER_SUB, DMA_PER_WAVE - s * DMA_PER_SUB) : 0;
+                const int nmem = nrd + ndma;
+                const int nslot = NMF > nmem ? NMF : nmem;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < nslot; ++i) {
+                    if (i < NMF) {
+                        const int u = i / 4, t = i % 4;
+                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][t], bf[s & 1][u],
+                                                                         acc[t][u], 0, 0, 0);
+                    }
+                    // memory slot i: reads on even slots, DMAs between
+                    int r = -1, d = -1;
+                    if (nrd > 0 && ndma > 0) {
+                        const int m = min(nrd, ndma);
+                        if (i < 2 * m) {
+                            if (i & 1) d = i / 2; else r = i / 2;
+                        } else if (i - m < nrd && nrd > ndma) {
+                            r = i - m;
+                        } else if (i - m < ndma && ndma > nrd) {
+                            d = i - m;
+                        }
+                    } else if (i < nrd) {
+                        r = i;
+                    } else if (i < ndma) {
+                        d = i;
+                    }
+                    if (r >= 0) read_one(wb, tb, s + 1, (s + 1) & 1, r);
+                    if (d >= 0) dma_one(s * DMA_PER_SUB + d, kt_t, kt_w, slot_t, slot_w);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (NTT > 0) {
-#pragma unroll
-                    for (int u = 0; u < NTT; ++u)
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][t], bf[s & 1][u],
-                                                                             acc[t][u], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // half of step kt+2's DMA per MFMA step
-                dma_step(nstage, kn, s * (DMA_PER_WAVE / 2), (s + 1) * (DMA_PER_WAVE / 2));
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
         wait_vm<0>();
@@ -275,7 +313,7 @@ unsigned tile_grid(int NT, int M) {
 
 template <bool DUAL>
 hipError_t launch(const StageArgs &a, int NT, hipStream_t s) {
-    const unsigned lds = NSTAGE * STAGE;  // 96 KB: above the 64 KB default, so opt in
+    const unsigned lds = LDS_BYTES;  // above the 64 KB default, so opt in
     hipError_t e = hipFuncSetAttribute((const void *)tile_kernel<DUAL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
