@@ -29,8 +29,10 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, TFLOP/s
 METRIC = "fused MoE TFLOP/s (useful 6·pairs·H·I) + % MFMA/HBM roofline, 1×MI355X"
-KERNEL_SOURCES = {"gate_up": ["rmoe_stream.hip", "rmoe_tile.hip", "rmoe_device.h"],
-                  "down": ["rmoe_stream.hip", "rmoe_tile.hip", "rmoe_device.h"]}
+# sources that define a variant's kernels: a traffic record is valid only for
+# the exact sources it was measured on
+KERNEL_SOURCES = {"stream": ["rmoe_stream.hip", "rmoe_device.h"],
+                  "tile": ["rmoe_tile.hip", "rmoe_device.h"]}
 
 
 def parse():
@@ -64,9 +66,9 @@ def calibrate_copy(mib: int, steps: int):
                       "bytes_written_per_launch": n * 2, "launches": steps}), flush=True)
 
 
-def kernel_src_hash(which: str) -> str:
+def kernel_src_hash(variant: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[which]:
+    for f in KERNEL_SOURCES[variant]:
         with open(os.path.join(ROOT, "mixture_experts_routed_grouped_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -97,15 +99,16 @@ def algorithmic(cfg, c, variant):
             "experts_active": e_act}
 
 
-def traffic_for(kernel: str, workload: str):
+def traffic_for(kernel: str, workload: str, variant: str):
     """Measured HBM bytes per launch from a committed rocprofv3 counter
-    summary, only if the kernel sources have not changed since."""
+    summary, only if it was taken on this variant and its kernel sources
+    have not changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_src_sha") != kernel_src_hash(kernel):
+    if rec.get("variant") != variant or rec.get("kernel_src_sha") != kernel_src_hash(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -232,8 +235,9 @@ def main():
         ach = alg["gate_up"]["flops"] / gu_s / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_F16_TFLOPS}
-    roof["kernel"] = "gate_up (" + ("stream_kernel<true,4>" if hbm_bound else "tile_kernel<true>") + ")"
-    roof["traffic"] = traffic_for("gate_up", cfg.name)
+    roof["kernel"] = "gate_up: " + ("stream_kernel<true,...> (LDS-DMA weight streaming)" if hbm_bound
+                                    else "tile_kernel<true> (256x256 LDS-tiled MFMA)")
+    roof["traffic"] = traffic_for("gate_up", cfg.name, resolved)
     total_bytes = alg["gate_up"]["bytes"] + alg["down"]["bytes"]
     result = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
