@@ -99,6 +99,41 @@ def algorithmic(cfg, c, variant):
             "experts_active": e_act}
 
 
+def aux_timings(cfg, inp, hid, out, reps=20):
+    """Average launch-to-completion time of the steps around the routed
+    kernels (outside the headline scope): the device-side contract build
+    from device top-k ids, the pack, and the combine."""
+    import torch
+    import mixture_experts_routed_grouped_amd as R
+    dev = inp.x.device
+    ids = torch.from_numpy(inp.topk_ids).to(dev)
+    topk_w = torch.from_numpy(inp.topk_w.reshape(-1).copy()).to(dev)
+    d = R.build_contract_device(ids, cfg.experts)
+    stacked = torch.empty((d["total_padded_tokens"], cfg.hidden), dtype=torch.float16, device=dev)
+    w_compact = torch.empty(d["pairs"], dtype=torch.float32, device=dev)
+    y = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.float16, device=dev)
+    steps = {
+        "contract_device": lambda: R.build_contract_device(ids, cfg.experts),
+        "pack": lambda: R.pack(inp.x, topk_w, d["padded_row_of_pair"], d["compact_pos_of_pair"],
+                               stacked, w_compact),
+        "combine": lambda: R.combine(out[:d["total_padded_tokens"]], d["padded_row_of_pair"],
+                                     cfg.top_k, y),
+    }
+    res = {}
+    for name, fn in steps.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / reps
+    return res
+
+
 def traffic_for(kernel: str, workload: str, variant: str):
     """Measured HBM bytes per launch from a committed rocprofv3 counter
     summary, only if it was taken on this variant and its kernel sources
@@ -264,6 +299,7 @@ def main():
         "latency_ms": stats_ms(step_ms),
         "device": torch.cuda.get_device_name(0),
     }
+    result["aux_kernels_us"] = aux_timings(cfg, inp, hid, out)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     else:

@@ -177,7 +177,10 @@ RMOE_API int rmoe_down_f16(const void *workspace, const void *down_w,
  * for p < num_tokens*top_k.  x [num_tokens, H] fp16 device, topk_weights
  * [num_tokens*top_k] fp32 device, maps int32 device, stacked [Tp, H] fp16
  * device, w_compact [pairs] fp32 device.  Other rows of stacked are not
- * written.  H must be a multiple of 8.
+ * written.  H must be a multiple of 8.  A pair whose padded row lies outside
+ * [0, total_padded_tokens) or whose compact position lies outside [0, pairs)
+ * (the device contract marks pairs with invalid expert ids with -1) moves
+ * nothing.
  */
 RMOE_API int rmoe_pack_f16(const void *x, const float *topk_weights,
                            const int32_t *padded_row_of_pair, const int32_t *compact_pos_of_pair,
@@ -189,10 +192,48 @@ RMOE_API int rmoe_pack_f16(const void *x, const float *topk_weights,
  * expert outputs of each token): y[t] = fp16( sum_j out[padded_row_of_pair
  * [t*top_k + j]] ) with the sum in fp32 in slot order j = 0..top_k-1.
  * out [Tp, H] fp16 device, y [num_tokens, H] fp16 device.  H multiple of 8.
+ * Slots whose padded row lies outside [0, total_padded_tokens) add nothing.
  */
 RMOE_API int rmoe_combine_f16(const void *out, const int32_t *padded_row_of_pair,
                               int64_t num_tokens, int32_t top_k, int64_t hidden, void *y,
                               int64_t total_padded_tokens, void *stream);
+
+/*
+ * Device-side dispatch contract (same tables as rmoe_build_contract, the
+ * tutorial page "moe_dispatch_contract.py", build_contract; computed on the
+ * GPU so that the routing never goes through the host -- the write-up's
+ * host-overhead list, section 2.7, names the bincount().cpu() sync and the
+ * metadata upload).
+ *   topk_ids [num_tokens, top_k] int32 on the device.  Pair p = t*top_k + j;
+ *   pairs are sorted by expert, stably (ties keep ascending p), so the tables
+ *   are identical to the host builder's.
+ * Outputs (device, caller-allocated): group_sizes [E], group_offsets [E+1],
+ *   group_padded_offsets [E+1], group_idx_for_bx [capacity_blocks] (filled
+ *   for bx < *num_blocks_m), order [pairs], padded_row_of_pair [pairs],
+ *   compact_pos_of_pair [pairs], *bad_ids (one int32).  *num_blocks_m (host)
+ *   = ceil(pairs/128) + E is returned at once, before the work runs.
+ * Ids outside [0, E) are not an error the call can report synchronously:
+ *   such pairs are left out of every table (entries of order past the valid
+ *   pairs are not written), get -1 in padded_row_of_pair and
+ *   compact_pos_of_pair (rmoe_pack_f16 / rmoe_combine_f16 skip them), and
+ *   their count lands in *bad_ids.
+ * workspace: device scratch of rmoe_contract_workspace_bytes(pairs, E)
+ *   bytes, caller-owned, contents irrelevant on entry.
+ * Asynchronous on `stream` (4 small launches); allocates nothing.  Errors
+ *   (returned before any launch): RMOE_ERR_INVALID_ARGUMENT (negative sizes,
+ *   NULL pointers, pairs or padded rows beyond int32), RMOE_ERR_UNSUPPORTED_
+ *   SHAPE (E > 8192), RMOE_ERR_CAPACITY (capacity_blocks or workspace too
+ *   small), RMOE_ERR_MISALIGNED (pointers not 4-byte aligned).
+ */
+RMOE_API size_t rmoe_contract_workspace_bytes(int64_t num_pairs, int32_t num_experts);
+RMOE_API int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                                        int32_t num_experts, int32_t *group_sizes,
+                                        int32_t *group_offsets, int32_t *group_padded_offsets,
+                                        int32_t *group_idx_for_bx, int64_t capacity_blocks,
+                                        int32_t *num_blocks_m, int32_t *order,
+                                        int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair,
+                                        int32_t *bad_ids, void *workspace, size_t workspace_bytes,
+                                        void *stream);
 
 #ifdef __cplusplus
 }

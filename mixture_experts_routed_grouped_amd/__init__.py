@@ -49,6 +49,9 @@ _SIGS = {
     "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
     "rmoe_combine_f16": ([_P, _P, _I64, _I32, _I64, _P, _I64, _P], ctypes.c_int),
+    "rmoe_contract_workspace_bytes": ([_I64, _I32], ctypes.c_size_t),
+    "rmoe_build_contract_device": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                    _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 
@@ -251,6 +254,48 @@ def combine(out, padded_row_of_pair, top_k, y, stream=None):
         _dev(out, torch.float16, "out"), _dev(padded_row_of_pair, torch.int32, "padded_row_of_pair"),
         T, int(top_k), H, _dev(y, torch.float16, "y"), out.shape[0], _stream(out, stream))
     _check(st, "rmoe_combine_f16")
+
+
+def contract_workspace_bytes(num_pairs: int, num_experts: int) -> int:
+    """Device scratch bytes ``build_contract_device`` needs."""
+    return int(lib().rmoe_contract_workspace_bytes(num_pairs, num_experts))
+
+
+def build_contract_device(topk_ids, num_experts: int, stream=None) -> dict:
+    """The dispatch contract built on the GPU from device top-k ids
+    ``[T, k]`` int32.  Returns device int32 tensors ``group_sizes``,
+    ``group_offsets``, ``group_padded_offsets``, ``group_idx_for_bx``,
+    ``order``, ``padded_row_of_pair``, ``compact_pos_of_pair``, ``bad_ids``
+    (one entry: pairs with an expert id outside [0, E), which the tables
+    leave out) and the host ints ``num_blocks_m``, ``total_padded_tokens``
+    and ``pairs``.  Asynchronous on ``stream``; no host round trip."""
+    torch = _torch()
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
+    T, k = topk_ids.shape
+    pairs, E = T * k, int(num_experts)
+    M = -(-pairs // BLOCK_M) + E
+    dev = topk_ids.device
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=dev)[:n]
+    out = {"group_sizes": i32(E), "group_offsets": i32(E + 1), "group_padded_offsets": i32(E + 1),
+           "group_idx_for_bx": i32(M), "order": i32(pairs), "padded_row_of_pair": i32(pairs),
+           "compact_pos_of_pair": i32(pairs), "bad_ids": i32(1)}
+    nbytes = contract_workspace_bytes(pairs, E)
+    if nbytes == 0:
+        raise RmoeError(f"device contract: unsupported expert count {E}")
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=dev)
+    nb = ctypes.c_int32(0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib().rmoe_build_contract_device(
+        _dev(topk_ids.contiguous(), torch.int32, "topk_ids") if pairs else ctypes.c_void_p(0),
+        T, k, E, ptr(out["group_sizes"]), ptr(out["group_offsets"]),
+        ptr(out["group_padded_offsets"]), ptr(out["group_idx_for_bx"]), M, ctypes.byref(nb),
+        ptr(out["order"]), ptr(out["padded_row_of_pair"]), ptr(out["compact_pos_of_pair"]),
+        ptr(out["bad_ids"]), ptr(ws), nbytes, _stream(topk_ids, stream))
+    _check(st, "rmoe_build_contract_device")
+    out["_workspace"] = ws  # keeps the scratch alive until the stream has used it
+    out.update(num_blocks_m=nb.value, total_padded_tokens=BLOCK_M * nb.value, pairs=pairs)
+    return out
 
 
 _WORKSPACE = {}

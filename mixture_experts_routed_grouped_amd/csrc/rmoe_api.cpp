@@ -16,6 +16,7 @@ constexpr int64_t B = RMOE_BLOCK_M;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+constexpr int32_t kMaxDeviceExperts = 8192;  // the device contract keeps per-expert tables in LDS
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -280,10 +281,10 @@ int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,
     if (!aligned16(x) || !aligned16(stacked) || !aligned4(topk_weights) || !aligned4(prow) ||
         !aligned4(cpos) || !aligned4(w_compact))
         return RMOE_ERR_MISALIGNED;
-    (void)total_padded_tokens;
     return to_status(rmoe::launch_pack(static_cast<const _Float16 *>(x), topk_weights, prow, cpos,
-                                       pairs, top_k, hidden, static_cast<_Float16 *>(stacked),
-                                       w_compact, static_cast<hipStream_t>(stream)));
+                                       pairs, top_k, hidden, total_padded_tokens,
+                                       static_cast<_Float16 *>(stacked), w_compact,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int rmoe_combine_f16(const void *out, const int32_t *prow, int64_t num_tokens, int32_t top_k,
@@ -294,10 +295,51 @@ int rmoe_combine_f16(const void *out, const int32_t *prow, int64_t num_tokens, i
     if (num_tokens == 0) return RMOE_OK;
     if (!y || (top_k > 0 && (!out || !prow))) return RMOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(y) || !aligned16(out) || !aligned4(prow)) return RMOE_ERR_MISALIGNED;
-    (void)total_padded_tokens;
     return to_status(rmoe::launch_combine(static_cast<const _Float16 *>(out), prow, num_tokens,
-                                          top_k, hidden, static_cast<_Float16 *>(y),
-                                          static_cast<hipStream_t>(stream)));
+                                          top_k, hidden, total_padded_tokens,
+                                          static_cast<_Float16 *>(y), static_cast<hipStream_t>(stream)));
+}
+
+// ---- device-side contract ------------------------------------------------
+
+size_t rmoe_contract_workspace_bytes(int64_t num_pairs, int32_t num_experts) {
+    if (num_pairs < 0 || num_experts < 1 || num_experts > kMaxDeviceExperts) return 0;
+    const int64_t nch = rmoe::contract_chunks(num_pairs);
+    const size_t n = (size_t)(nch * ((int64_t)num_experts + 1));
+    return n > 0 ? n * sizeof(int32_t) : 4;
+}
+
+int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                               int32_t num_experts, int32_t *group_sizes, int32_t *group_offsets,
+                               int32_t *group_padded_offsets, int32_t *group_idx_for_bx,
+                               int64_t capacity_blocks, int32_t *num_blocks_m, int32_t *order,
+                               int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair,
+                               int32_t *bad_ids, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    if (num_tokens < 0 || top_k < 0 || num_experts < 1 || !num_blocks_m) return RMOE_ERR_INVALID_ARGUMENT;
+    if (num_experts > kMaxDeviceExperts) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    const int64_t pairs = num_tokens * top_k;
+    if (pairs > INT32_MAX / 2) return RMOE_ERR_INVALID_ARGUMENT;
+    const int64_t M = ceil_div(pairs, B) + num_experts;
+    if (M * B > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!group_sizes || !group_offsets || !group_padded_offsets || !group_idx_for_bx || !bad_ids ||
+        !workspace)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (pairs > 0 && (!topk_ids || !order || !padded_row_of_pair || !compact_pos_of_pair))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (capacity_blocks < M) return RMOE_ERR_CAPACITY;
+    if (workspace_bytes < rmoe_contract_workspace_bytes(pairs, num_experts)) return RMOE_ERR_CAPACITY;
+    if (!aligned4(topk_ids) || !aligned4(group_sizes) || !aligned4(group_offsets) ||
+        !aligned4(group_padded_offsets) || !aligned4(group_idx_for_bx) || !aligned4(order) ||
+        !aligned4(padded_row_of_pair) || !aligned4(compact_pos_of_pair) || !aligned4(bad_ids) ||
+        !aligned4(workspace))
+        return RMOE_ERR_MISALIGNED;
+    *num_blocks_m = (int32_t)M;
+    return to_status(rmoe::launch_contract(topk_ids, pairs, num_experts, (int32_t)M, group_sizes,
+                                           group_offsets, group_padded_offsets, group_idx_for_bx,
+                                           order, padded_row_of_pair, compact_pos_of_pair, bad_ids,
+                                           static_cast<int32_t *>(workspace),
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -34,9 +34,16 @@ hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s);
 hipError_t launch_tile_down(const StageArgs &a, hipStream_t s);
 
 hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,
-                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H,
+                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H, int64_t Tp,
                        _Float16 *stacked, float *w_compact, hipStream_t s);
 hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, int32_t top_k,
-                          int64_t H, _Float16 *y, hipStream_t s);
+                          int64_t H, int64_t Tp, _Float16 *y, hipStream_t s);
+
+// Device-side contract build.  ws holds contract_chunks(pairs) * (E + 1)
+// int32 of scratch.
+int64_t contract_chunks(int64_t pairs);
+hipError_t launch_contract(const int32_t *ids, int64_t pairs, int32_t E, int32_t M, int32_t *gs,
+                           int32_t *go, int32_t *gpo, int32_t *gidx, int32_t *order, int32_t *prow,
+                           int32_t *cpos, int32_t *bad, int32_t *ws, hipStream_t s);
 
 }  // namespace rmoe

@@ -8,12 +8,14 @@
 namespace rmoe {
 namespace {
 
-// stacked[prow[p]] = x[p / k]; w_compact[cpos[p]] = topk_w[p]
+// stacked[prow[p]] = x[p / k]; w_compact[cpos[p]] = topk_w[p].  A pair whose
+// table entry lies outside [0, Tp) or [0, pairs) (a pair the device contract
+// left out for an out-of-range expert id) moves nothing.
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ x,
                                                    const float *__restrict__ topk_w,
                                                    const int32_t *__restrict__ prow,
                                                    const int32_t *__restrict__ cpos, int64_t pairs,
-                                                   int32_t k, int64_t chunks_per_row,
+                                                   int32_t k, int64_t chunks_per_row, int64_t Tp,
                                                    _Float16 *__restrict__ stacked,
                                                    float *__restrict__ w_compact) {
     const int64_t total = pairs * chunks_per_row;
@@ -22,15 +24,20 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = i / chunks_per_row, c = i - p * chunks_per_row;
         const int64_t t = p / k;
-        *(h8 *)(stacked + (int64_t)prow[p] * H + 8 * c) = *(const h8 *)(x + t * H + 8 * c);
-        if (c == 0) w_compact[cpos[p]] = topk_w[p];
+        const int64_t r = prow[p];
+        if (r >= 0 && r < Tp) *(h8 *)(stacked + r * H + 8 * c) = *(const h8 *)(x + t * H + 8 * c);
+        if (c == 0) {
+            const int64_t q = cpos[p];
+            if (q >= 0 && q < pairs) w_compact[q] = topk_w[p];
+        }
     }
 }
 
-// y[t] = fp16(sum_j out[prow[t*k + j]]), fp32 sum in slot order
+// y[t] = fp16(sum_j out[prow[t*k + j]]), fp32 sum in slot order; slots whose
+// padded row lies outside [0, Tp) contribute nothing
 __global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict__ out,
                                                       const int32_t *__restrict__ prow, int64_t T,
-                                                      int32_t k, int64_t chunks_per_row,
+                                                      int32_t k, int64_t chunks_per_row, int64_t Tp,
                                                       _Float16 *__restrict__ y) {
     const int64_t total = T * chunks_per_row;
     const int64_t H = chunks_per_row * 8;
@@ -39,7 +46,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict
         const int64_t t = i / chunks_per_row, c = i - t * chunks_per_row;
         float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
-            const h8 v = *(const h8 *)(out + (int64_t)prow[t * k + j] * H + 8 * c);
+            const int64_t r = prow[t * k + j];
+            if (r < 0 || r >= Tp) continue;
+            const h8 v = *(const h8 *)(out + r * H + 8 * c);
 #pragma unroll
             for (int q = 0; q < 8; ++q) s[q] += (float)v[q];
         }
@@ -59,21 +68,21 @@ unsigned grid_for(int64_t total) {
 }  // namespace
 
 hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,
-                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H,
+                       const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H, int64_t Tp,
                        _Float16 *stacked, float *w_compact, hipStream_t s) {
     if (pairs == 0) return hipSuccess;
     const int64_t cpr = H / 8;
     hipLaunchKernelGGL(pack_kernel, dim3(grid_for(pairs * cpr)), dim3(256), 0, s, x, topk_w, prow,
-                       cpos, pairs, top_k, cpr, stacked, w_compact);
+                       cpos, pairs, top_k, cpr, Tp, stacked, w_compact);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, int32_t top_k,
-                          int64_t H, _Float16 *y, hipStream_t s) {
+                          int64_t H, int64_t Tp, _Float16 *y, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int64_t cpr = H / 8;
     hipLaunchKernelGGL(combine_kernel, dim3(grid_for(T * cpr)), dim3(256), 0, s, out, prow, T,
-                       top_k, cpr, y);
+                       top_k, cpr, Tp, y);
     return hipGetLastError();
 }
 

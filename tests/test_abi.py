@@ -130,3 +130,34 @@ def test_argument_errors_without_gpu():
     assert L.rmoe_combine_f16(fake, fake, -1, 2, 16, fake, 640, None) == -1
     assert L.rmoe_workspace_bytes(640, 128) == 640 * 128 * 2
     assert R.status_str(-5).startswith("tables violate")
+
+
+def test_device_contract_argument_errors_without_gpu():
+    """The device contract's argument checks also run before any HIP call."""
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10002)
+    nb = ctypes.c_int32(-1)
+    ws_ok = L.rmoe_contract_workspace_bytes(18, 4)
+    # 18 pairs fit one 2048-pair chunk: (E + 1) int32 of per-chunk counts
+    assert ws_ok == 1 * (4 + 1) * 4
+    assert L.rmoe_contract_workspace_bytes(131072, 128) == 64 * 129 * 4
+    assert L.rmoe_contract_workspace_bytes(10, 0) == 0
+    assert L.rmoe_contract_workspace_bytes(10, 8193) == 0
+
+    def dev(T=9, k=2, E=4, cap=5, ws=ws_ok, ids=fake, gs=fake, bad=fake, work=fake, nbp=ctypes.byref(nb)):
+        return L.rmoe_build_contract_device(ids, T, k, E, gs, fake, fake, fake, cap, nbp, fake, fake,
+                                            fake, bad, work, ws, None)
+
+    assert dev(T=-1) == -1
+    assert dev(E=0) == -1
+    assert dev(E=8193, cap=10 ** 6) == -2                 # expert tables live in LDS
+    assert dev(ids=None) == -1
+    assert dev(gs=None) == -1
+    assert dev(bad=None) == -1
+    assert dev(work=None) == -1
+    assert dev(nbp=None) == -1
+    assert dev(cap=4) == -6                               # ceil(18/128) + 4 = 5 blocks needed
+    assert dev(ws=ws_ok - 1) == -6                        # workspace too small
+    assert dev(ids=odd) == -3
+    assert nb.value == -1                                 # nothing written on an error
