@@ -99,25 +99,44 @@ def algorithmic(cfg, c, variant):
             "experts_active": e_act}
 
 
-def aux_timings(cfg, inp, hid, out, reps=20):
-    """Average launch-to-completion time of the steps around the routed
-    kernels (outside the headline scope): the device-side contract build
-    from device top-k ids, the pack, and the combine."""
+def aux_timings(cfg, inp, hid, out, variant, reps=20):
+    """Average time per call of the steps around the routed kernels (outside
+    the headline scope): the router (synthetic gate [E, H]), the device-side
+    contract build from device top-k ids, the pack, the combine, and the
+    whole layer -- router, device contract, pack, both expert kernels,
+    combine -- with no host round trip."""
     import torch
     import mixture_experts_routed_grouped_amd as R
+    import workloads
     dev = inp.x.device
     ids = torch.from_numpy(inp.topk_ids).to(dev)
     topk_w = torch.from_numpy(inp.topk_w.reshape(-1).copy()).to(dev)
+    wr = workloads.make_router_weight(cfg, device=dev)
     d = R.build_contract_device(ids, cfg.experts)
     stacked = torch.empty((d["total_padded_tokens"], cfg.hidden), dtype=torch.float16, device=dev)
     w_compact = torch.empty(d["pairs"], dtype=torch.float32, device=dev)
     y = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.float16, device=dev)
+    r_ids = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.int32, device=dev)
+    r_w = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev)
+
+    def layer():
+        R.router(inp.x, wr, cfg.top_k, r_ids, r_w)
+        c = R.build_contract_device(r_ids, cfg.experts)
+        R.pack(inp.x, r_w.reshape(-1), c["padded_row_of_pair"], c["compact_pos_of_pair"], stacked,
+               w_compact)
+        R.gate_up(stacked, inp.wg, inp.wu, c["group_sizes"], c["group_padded_offsets"],
+                  c["group_idx_for_bx"], hid, variant=variant)
+        R.down(hid, inp.wd, w_compact, c["group_sizes"], c["group_offsets"],
+               c["group_padded_offsets"], c["group_idx_for_bx"], out, variant=variant)
+        R.combine(out, c["padded_row_of_pair"], cfg.top_k, y)
+
     steps = {
+        "router": lambda: R.router(inp.x, wr, cfg.top_k, r_ids, r_w),
         "contract_device": lambda: R.build_contract_device(ids, cfg.experts),
         "pack": lambda: R.pack(inp.x, topk_w, d["padded_row_of_pair"], d["compact_pos_of_pair"],
                                stacked, w_compact),
-        "combine": lambda: R.combine(out[:d["total_padded_tokens"]], d["padded_row_of_pair"],
-                                     cfg.top_k, y),
+        "combine": lambda: R.combine(out, d["padded_row_of_pair"], cfg.top_k, y),
+        "layer_e2e": layer,
     }
     res = {}
     for name, fn in steps.items():
@@ -299,7 +318,7 @@ def main():
         "latency_ms": stats_ms(step_ms),
         "device": torch.cuda.get_device_name(0),
     }
-    result["aux_kernels_us"] = aux_timings(cfg, inp, hid, out)
+    result["aux_kernels_us"] = aux_timings(cfg, inp, hid, out, resolved)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     else:

@@ -235,6 +235,27 @@ RMOE_API int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tok
                                         int32_t *bad_ids, void *workspace, size_t workspace_bytes,
                                         void *stream);
 
+/*
+ * Router (write-up "MetaX-TileLang工具链", section 2.4: the reference router
+ * is a linear gate, a softmax, a top-k):
+ *   logits[t, e] = sum_h x[t, h] * router_w[e, h]   (fp32 accumulation)
+ *   p[t, :] = softmax(logits[t, :]) over the E experts (fp32)
+ *   topk_ids[t, j], topk_weights[t, j], j < top_k: the top_k largest p[t, e]
+ *   in decreasing order, equal scores by ascending expert index; the
+ *   weights are the probabilities themselves (no renormalisation is stated).
+ * x [num_tokens, hidden] fp16 device, router_w [E, hidden] fp16 device,
+ * topk_ids [num_tokens, top_k] int32 device, topk_weights [num_tokens,
+ * top_k] fp32 device; all caller-owned, contiguous.  The outputs feed
+ * rmoe_build_contract_device and rmoe_pack_f16 directly.
+ * Shapes: hidden % 64 == 0, 1 <= E <= 256, 0 <= top_k <= min(E, 32).
+ * Asynchronous on `stream`, one launch, allocates nothing.  Errors:
+ * RMOE_ERR_INVALID_ARGUMENT, RMOE_ERR_UNSUPPORTED_SHAPE, RMOE_ERR_MISALIGNED
+ * (fp16 tensors 16-byte, outputs 4-byte aligned), RMOE_ERR_LAUNCH.
+ */
+RMOE_API int rmoe_router_f16(const void *x, const void *router_w, int64_t num_tokens,
+                             int64_t hidden, int32_t num_experts, int32_t top_k,
+                             int32_t *topk_ids, float *topk_weights, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,7 @@ _SIGS = {
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
     "rmoe_combine_f16": ([_P, _P, _I64, _I32, _I64, _P, _I64, _P], ctypes.c_int),
     "rmoe_contract_workspace_bytes": ([_I64, _I32], ctypes.c_size_t),
+    "rmoe_router_f16": ([_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "rmoe_build_contract_device": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                     _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
@@ -254,6 +255,26 @@ def combine(out, padded_row_of_pair, top_k, y, stream=None):
         _dev(out, torch.float16, "out"), _dev(padded_row_of_pair, torch.int32, "padded_row_of_pair"),
         T, int(top_k), H, _dev(y, torch.float16, "y"), out.shape[0], _stream(out, stream))
     _check(st, "rmoe_combine_f16")
+
+
+def router(x, router_w, top_k: int, topk_ids=None, topk_weights=None, stream=None):
+    """Top-k expert ids (int32) and softmax scores (fp32) of ``x @ router_w^T``
+    for x [T, H] and router_w [E, H] fp16 device tensors; returns
+    ``(topk_ids, topk_weights)``, both [T, top_k]."""
+    torch = _torch()
+    T, H = x.shape
+    E = router_w.shape[0]
+    if router_w.dim() != 2 or router_w.shape[1] != H:
+        raise ValueError("router_w must be [E, H]")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    st = lib().rmoe_router_f16(_dev(x, torch.float16, "x"), _dev(router_w, torch.float16, "router_w"),
+                               T, H, E, int(top_k), _dev(topk_ids, torch.int32, "topk_ids"),
+                               _dev(topk_weights, torch.float32, "topk_weights"), _stream(x, stream))
+    _check(st, "rmoe_router_f16")
+    return topk_ids, topk_weights
 
 
 def contract_workspace_bytes(num_pairs: int, num_experts: int) -> int:

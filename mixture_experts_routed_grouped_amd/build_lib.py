@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librmoe.so")
-SOURCES = ["rmoe_api.cpp", "rmoe_stream.hip", "rmoe_tile.hip", "rmoe_pack.hip", "rmoe_contract.hip"]
+SOURCES = ["rmoe_api.cpp", "rmoe_stream.hip", "rmoe_tile.hip", "rmoe_pack.hip", "rmoe_contract.hip", "rmoe_router.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

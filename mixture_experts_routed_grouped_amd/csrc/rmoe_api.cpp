@@ -342,4 +342,22 @@ int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tokens, int3
                                            static_cast<hipStream_t>(stream)));
 }
 
+// ---- router ----------------------------------------------------------------
+
+int rmoe_router_f16(const void *x, const void *router_w, int64_t num_tokens, int64_t hidden,
+                    int32_t num_experts, int32_t top_k, int32_t *topk_ids, float *topk_weights,
+                    void *stream) {
+    if (num_tokens < 0 || hidden <= 0 || num_experts < 1 || top_k < 0 || top_k > num_experts)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (num_experts > 256 || top_k > 32 || hidden % 64 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    if (num_tokens == 0 || top_k == 0) return RMOE_OK;
+    if (!x || !router_w || !topk_ids || !topk_weights) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(router_w) || !aligned4(topk_ids) || !aligned4(topk_weights))
+        return RMOE_ERR_MISALIGNED;
+    return to_status(rmoe::launch_router(static_cast<const _Float16 *>(x),
+                                         static_cast<const _Float16 *>(router_w), num_tokens, hidden,
+                                         num_experts, top_k, topk_ids, topk_weights,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

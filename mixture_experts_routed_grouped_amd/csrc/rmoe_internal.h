@@ -39,6 +39,10 @@ hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *pr
 hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, int32_t top_k,
                           int64_t H, int64_t Tp, _Float16 *y, hipStream_t s);
 
+// Router: top-k ids and softmax scores of x W^T (E <= 256).
+hipError_t launch_router(const _Float16 *x, const _Float16 *w, int64_t T, int64_t H, int32_t E,
+                         int32_t k, int32_t *ids, float *vals, hipStream_t s);
+
 // Device-side contract build.  ws holds contract_chunks(pairs) * (E + 1)
 // int32 of scratch.
 int64_t contract_chunks(int64_t pairs);

@@ -161,3 +161,24 @@ def test_device_contract_argument_errors_without_gpu():
     assert dev(ws=ws_ok - 1) == -6                        # workspace too small
     assert dev(ids=odd) == -3
     assert nb.value == -1                                 # nothing written on an error
+
+
+def test_router_argument_errors_without_gpu():
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+
+    def rt(T=64, H=256, E=8, k=2, x=fake, ids=fake):
+        return L.rmoe_router_f16(x, fake, T, H, E, k, ids, fake, None)
+
+    assert rt(T=-1) == -1
+    assert rt(E=0) == -1
+    assert rt(k=9) == -1                                  # k > E
+    assert rt(k=-1) == -1
+    assert rt(E=257, k=2) == -2                           # E above the kernel's 256
+    assert rt(E=64, k=33) == -2
+    assert rt(H=96) == -2                                 # H not a multiple of 64
+    assert rt(x=None) == -1
+    assert rt(x=odd) == -3
+    assert rt(T=0, x=None) == 0                           # nothing to do
+    assert rt(k=0, ids=None) == 0

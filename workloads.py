@@ -151,3 +151,10 @@ def make_inputs(cfg: Config, device="cpu", topk_ids: np.ndarray | None = None) -
     wu = _normal_f16((E, I, H), 1.0 / math.sqrt(H), cfg.seed, 3, device, chunks=ch)
     wd = _normal_f16((E, H, I), 1.0 / math.sqrt(I), cfg.seed, 4, device, chunks=ch)
     return Inputs(cfg, topk_ids, topk_w, x, wg, wu, wd)
+
+
+def make_router_weight(cfg: Config, device="cpu") -> torch.Tensor:
+    """Synthetic router gate [E, H] fp16, N(0, 1/H): with x ~ N(0, 1) the
+    logits are ~N(0, 1), a spread of scores like a trained router's."""
+    return _normal_f16((cfg.experts, cfg.hidden), 1.0 / math.sqrt(cfg.hidden), cfg.seed, 5, device)
+
