@@ -59,18 +59,21 @@ struct StreamCfg {
     static constexpr int RING = KS * WAVE_LDS;
     static constexpr int RED = KS * NM * 16 * 64 * 4;  // partial sums of one tile
     static constexpr int LDS_BYTES = RING > RED ? RING : RED;
-    static constexpr int DMA_PER_CHUNK = 4 * (NM + 1);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-    static_assert((D - 1) * DMA_PER_CHUNK < 64, "vmcnt range");
+    static_assert((D - 1) * 4 * (NM + 1) < 64, "vmcnt range");
 };
 
 // One pass: the 32-token tile starting at row p0 of block bx against the 32
-// features n0.. of the block's expert, over the whole K.
-template <bool DUAL, int KS, int D>
+// features n0.. of the block's expert, over the whole K.  Only the first
+// 8*TD token rows of the tile are moved (TD = ceil(valid rows / 8)): LDS rows
+// past them keep stale values, which only reach MFMA output columns of
+// tokens that are never stored.
+template <bool DUAL, int KS, int D, int TD>
 __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo &bi, int bx, int p0,
                                             int n0, unsigned char *smem, int wave, int lane) {
     using C = StreamCfg<DUAL, KS, D>;
     constexpr int NM = C::NM;
+    constexpr int DMA_PER_CHUNK = 4 * NM + TD;
     const int64_t K = a.K, N = a.N;
     const int lr = lane & 31, lh = lane >> 5;
 
@@ -107,7 +110,7 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
 #pragma unroll
         for (int m = 0; m <= NM; ++m)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < (m == NM ? TD : 4); ++j)
                 dma16(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
     };
 
@@ -125,7 +128,7 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
             // repeats land in slots no later chunk reads), then wait for
             // chunk i, the oldest in flight
             dma_chunk(min(i + D - 1, n - 1), (i + D - 1) % D);
-            wait_vm<(D - 1) * C::DMA_PER_CHUNK>();
+            wait_vm<(D - 1) * DMA_PER_CHUNK>();
             const unsigned char *slot = wring + (i % D) * C::SLOT;
             h8 af[NM][4], bf[4];
 #pragma unroll
@@ -195,7 +198,14 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * MF;
-    for (int p0 = 0; p0 < bi.rows; p0 += 32) stream_pass<DUAL, KS, D>(a, bi, bx, p0, n0, smem, wave, lane);
+    for (int p0 = 0; p0 < bi.rows; p0 += 32) {
+        switch ((min(bi.rows - p0, 32) + 7) / 8) {  // token DMA rows of this pass, in 8s
+            case 1: stream_pass<DUAL, KS, D, 1>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            case 2: stream_pass<DUAL, KS, D, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            case 3: stream_pass<DUAL, KS, D, 3>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            default: stream_pass<DUAL, KS, D, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
+        }
+    }
 }
 
 template <bool DUAL, int KS, int D>
