@@ -34,9 +34,12 @@ __device__ __forceinline__ BlockInfo block_info(const int32_t *__restrict__ gs,
     return b;
 }
 
-// silu(g) = g * sigmoid(g) = g / (1 + e^-g), with the hardware exp2.
+// silu(g) = g * sigmoid(g) = g / (1 + e^-g), with the hardware exp2 and
+// reciprocal (each ~1 ulp of fp32; the result is rounded to fp16, whose ulp
+// is 2^13 times coarser).  For g -> -inf, e^-g -> inf and the reciprocal
+// -> 0, so silu -> -0 as it should.
 __device__ __forceinline__ float silu(float g) {
-    return g / (1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
 }
 
 __device__ __forceinline__ h4 to_h4(float a, float b, float c, float d) {

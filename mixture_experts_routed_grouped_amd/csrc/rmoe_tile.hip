@@ -21,9 +21,9 @@
 // XOR-swizzled per row so that MFMA operand reads (ds_read_b128) hit
 // distinct banks.  The 160 KB of LDS hold five 32 KB slots -- one K step of
 // 256 rows each: three for weights and two for tokens -- so weight DMAs run
-// two steps ahead of the MFMAs and token DMAs one step.  Weights are the
+// two steps ahead of the MFMAs and token DMAs one step (weights are the
 // first-touch stream from HBM; tokens are shared by the concurrently running
-// slices of a locality group and mostly hit L2.  Within a step the memory
+// slices of a locality group, so more of them hit L2).  Within a step the memory
 // instructions (the next sub-step's operand reads, the DMAs) are issued one
 // after each MFMA, so they leave the in-order wave while the matrix core is
 // busy.  The waits are explicit (vmcnt) and the barrier is a bare s_barrier,
@@ -51,28 +51,16 @@ constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
 constexpr int RPD = 64 / CPR;   // rows per 1 KB DMA instruction (8)
 constexpr int SROWS = 256;      // rows per slot: 256 weight rows or 256 tokens
 constexpr int SLOT = SROWS * ROWB;  // 32 KB
-#ifndef RMOE_TILE_WSLOTS
-#define RMOE_TILE_WSLOTS 3
-#endif
-#ifndef RMOE_TILE_TSLOTS
-#define RMOE_TILE_TSLOTS 2
-#endif
-constexpr int NWS = RMOE_TILE_WSLOTS;  // weight slots: weight DMA runs NWS-1 steps ahead
-constexpr int NTS = RMOE_TILE_TSLOTS;  // token slots: token DMA runs NTS-1 steps ahead
-static_assert(NWS >= NTS && NTS >= 2, "slot counts");
+constexpr int NWS = 3;  // weight slots: weight DMA runs two steps ahead
+constexpr int NTS = 2;  // token slots: token DMA runs one step ahead
 static_assert((NWS + NTS) * SLOT <= 160 * 1024, "LDS slots exceed 160 KB");
 constexpr int LDS_BYTES = (NWS + NTS) * SLOT;
-constexpr int DMA_HALF = SROWS / RPD / 4;  // DMAs per wave per slot fill (8)
+constexpr int DMA_HALF = SROWS / RPD / 4;   // DMAs per wave per slot fill (8)
 constexpr int DMA_PER_WAVE = 2 * DMA_HALF;  // per step: token fill, then weight fill
 constexpr int SUB = BK / 16;                // MFMA sub-steps per K step
-// vmcnt a wave may leave outstanding at the top of step k: the DMAs issued
-// after the last one step k needs (token step k when NWS > NTS)
-constexpr int VM_ALLOW = NWS > NTS ? DMA_HALF + DMA_PER_WAVE * (NTS - 2) : DMA_PER_WAVE * (NTS - 2);
-#ifndef RMOE_TILE_SPREAD
-#define RMOE_TILE_SPREAD 4
-#endif
-constexpr int DMA_SPREAD = RMOE_TILE_SPREAD;  // sub-steps a step's DMAs are spread over
-constexpr int DMA_PER_SUB = (DMA_PER_WAVE + DMA_SPREAD - 1) / DMA_SPREAD;
+// vmcnt a wave may leave outstanding when it publishes step k+1: the weight
+// fill of step k+2, issued after the token fill of step k+1
+constexpr int VM_ALLOW = DMA_HALF;
 
 // Work item of workgroup w in an order that keeps operand sharing inside one
 // XCD's L2.  Items (weight slice nt, block bx) are listed group by group:
@@ -180,84 +168,97 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
 
     const int nk = (int)(K / BK);
 
-    // One MFMA sub-step is 4 x NTT MFMAs (K = 16).  The memory instructions
-    // of a sub-step -- the LDS operand reads of the next sub-step and this
-    // sub-step's share of the DMA -- are issued one after each MFMA, so they
-    // leave the wave while the matrix core is busy instead of stalling it in
-    // a burst (a wave issues in order).
+    // The pipeline is rotated by one sub-step: the wait and barrier that
+    // publish step k+1 sit before the last sub-step of step k, so the LDS
+    // reads of step k+1's first sub-step overlap that sub-step's MFMAs
+    // instead of stalling every step start.  Group g(j) = the DMAs that
+    // refill step j's slots once every wave is done with them (tokens of
+    // step j+NTS, weights of step j+NWS), DPS per sub-step over the SUB
+    // sub-steps that follow the barrier retiring step j's reads.
     auto kloop = [&](auto ntt_c) {
         constexpr int NTT = decltype(ntt_c)::value;
         constexpr int NMF = 4 * NTT;  // MFMAs per sub-step
         constexpr int NRD = 4 + NTT;  // operand reads per sub-step
+        constexpr int DPS = DMA_PER_WAVE / SUB;
+        static_assert(DMA_PER_WAVE % SUB == 0, "DMA groups split evenly over the sub-steps");
         h8 af[2][4], bf[2][4];
-        auto read_one = [&](const unsigned char *wb, const unsigned char *tb, int s, int slot, int i) {
+        auto read_one = [&](const unsigned char *wb, const unsigned char *tb, int s, int buf, int i) {
             const int ch = 2 * s + lh;
             if (i < 4)
-                af[slot][i] = *(const h8 *)(wb + lds_off(wrow[i] + lr, ch));
+                af[buf][i] = *(const h8 *)(wb + lds_off(wrow[i] + lr, ch));
             else
-                bf[slot][i - 4] = *(const h8 *)(tb + lds_off(trow0 + 32 * (i - 4) + lr, ch));
+                bf[buf][i - 4] = *(const h8 *)(tb + lds_off(trow0 + 32 * (i - 4) + lr, ch));
         };
-        // prologue: the fills that steps -(NWS-1) .. -1 would issue, in
-        // the same order (tokens of step j + NTS-1, then weights of j + NWS-1)
+        // DMA d of group g(j); indices past the last step are clamped (the
+        // repeats land in slots no later step reads)
+        auto dma_g = [&](int j, int d) {
+            dma_one(d, min(j + NTS, nk - 1), min(j + NWS, nk - 1), (j + NTS) % NTS, (j + NWS) % NWS);
+        };
+        // one sub-step: MFMAs of sub-step sm (buffer sm & 1), interleaved with
+        // the reads of sub-step sr of (rw, rt) into buffer sr & 1 and DMAs
+        // dlo .. dlo + DPS - 1 of group gj
+        auto substep = [&](int sm, bool rd, const unsigned char *rw, const unsigned char *rt, int sr,
+                           bool dm, int gj, int dlo) {
+            const int nrd = (NTT > 0 && rd) ? NRD : 0;
+            const int ndma = dm ? DPS : 0;
+            const int nmem = nrd + ndma;
+            const int nslot = NMF > nmem ? NMF : nmem;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = -(NWS - 1); j < 0; ++j) {
-            const int tt = j + NTS - 1, tw = j + NWS - 1;
-            if (tt >= 0) {
-#pragma unroll
-                for (int d = 0; d < DMA_HALF; ++d) dma_one(d, min(tt, nk - 1), 0, tt % NTS, 0);
-            }
-#pragma unroll
-            for (int d = DMA_HALF; d < DMA_PER_WAVE; ++d) dma_one(d, 0, min(tw, nk - 1), 0, tw % NWS);
-        }
-        for (int kt = 0; kt < nk; ++kt) {
-            // tokens and weights of step kt landed (own DMAs), then all waves'
-            wait_vm<VM_ALLOW>();
-            bar();  // also: every wave finished reading step kt-1's slots
-            const unsigned char *wb = smem + (kt % NWS) * SLOT;
-            const unsigned char *tb = smem + (NWS + kt % NTS) * SLOT;
-            // this step's fills: clamped at the end so every step issues the
-            // same count (a repeat lands in a slot no later step reads)
-            const int kt_t = min(kt + NTS - 1, nk - 1), kt_w = min(kt + NWS - 1, nk - 1);
-            const int slot_t = (kt + NTS - 1) % NTS, slot_w = (kt + NWS - 1) % NWS;
-#pragma unroll
-            for (int i = 0; i < NRD; ++i)
-                if (NTT > 0) read_one(wb, tb, 0, 0, i);
-#pragma unroll
-            for (int s = 0; s < SUB; ++s) {
-                const int nrd = (NTT > 0 && s + 1 < SUB) ? NRD : 0;
-                const int ndma = s < DMA_SPREAD ? min(DMA_PER_SUB, DMA_PER_WAVE - s * DMA_PER_SUB) : 0;
-                const int nmem = nrd + ndma;
-                const int nslot = NMF > nmem ? NMF : nmem;
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < nslot; ++i) {
-                    if (i < NMF) {
-                        const int u = i / 4, t = i % 4;
-                        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][t], bf[s & 1][u],
-                                                                         acc[t][u], 0, 0, 0);
-                    }
-                    // memory slot i: reads on even slots, DMAs between
-                    int r = -1, d = -1;
-                    if (nrd > 0 && ndma > 0) {
-                        const int m = min(nrd, ndma);
-                        if (i < 2 * m) {
-                            if (i & 1) d = i / 2; else r = i / 2;
-                        } else if (i - m < nrd && nrd > ndma) {
-                            r = i - m;
-                        } else if (i - m < ndma && ndma > nrd) {
-                            d = i - m;
-                        }
-                    } else if (i < nrd) {
-                        r = i;
-                    } else if (i < ndma) {
-                        d = i;
-                    }
-                    if (r >= 0) read_one(wb, tb, s + 1, (s + 1) & 1, r);
-                    if (d >= 0) dma_one(s * DMA_PER_SUB + d, kt_t, kt_w, slot_t, slot_w);
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < nslot; ++i) {
+                if (i < NMF) {
+                    const int u = i / 4, t = i % 4;
+                    acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[sm & 1][t], bf[sm & 1][u],
+                                                                     acc[t][u], 0, 0, 0);
                 }
+                int r = -1, d = -1;  // memory slot i: reads on even slots, DMAs between
+                if (nrd > 0 && ndma > 0) {
+                    const int m = min(nrd, ndma);
+                    if (i < 2 * m) {
+                        if (i & 1) d = i / 2; else r = i / 2;
+                    } else if (i - m < nrd && nrd > ndma) {
+                        r = i - m;
+                    } else if (i - m < ndma && ndma > nrd) {
+                        d = i - m;
+                    }
+                } else if (i < nrd) {
+                    r = i;
+                } else if (i < ndma) {
+                    d = i;
+                }
+                if (r >= 0) read_one(rw, rt, sr, sr & 1, r);
+                if (d >= 0) dma_g(gj, dlo + d);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        // prologue: groups g(-3) (weights of step 0), g(-2) (tokens of step
+        // 0, weights of step 1) and the first part of g(-1) (tokens of step 1)
+#pragma unroll
+        for (int d = DMA_HALF; d < DMA_PER_WAVE; ++d) dma_g(-3, d);
+#pragma unroll
+        for (int d = 0; d < DMA_PER_WAVE; ++d) dma_g(-2, d);
+#pragma unroll
+        for (int d = 0; d < DPS; ++d) dma_g(-1, d);
+        wait_vm<DMA_HALF + DPS>();  // step 0 landed: only weights 1 and that part may be in flight
+        bar();
+        if constexpr (NTT > 0) {
+#pragma unroll
+            for (int i = 0; i < NRD; ++i) read_one(smem, smem + NWS * SLOT, 0, 0, i);
         }
+        for (int k = 0; k < nk; ++k) {
+            const unsigned char *wb = smem + (k % NWS) * SLOT;
+            const unsigned char *tb = smem + (NWS + k % NTS) * SLOT;
+            if (k > 0) substep(SUB - 1, true, wb, tb, 0, true, k - 1, 0);  // end of step k-1
+#pragma unroll
+            for (int s = 0; s + 1 < SUB; ++s) substep(s, true, wb, tb, s + 1, true, k - 1, DPS * (s + 1));
+            // publish step k+1 (tokens came with g(k-1); only the weights of
+            // step k+2 may still be in flight) and retire this wave's reads of
+            // step k, whose slots the next group refills
+            wait_vm<VM_ALLOW>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            bar();
+        }
+        substep(SUB - 1, false, nullptr, nullptr, 0, false, 0, 0);  // end of step nk-1
         wait_vm<0>();
     };
     switch (ntt) {
