@@ -268,18 +268,32 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
         case 1: kloop(std::integral_constant<int, 1>{}); break;
         default: kloop(std::integral_constant<int, 0>{}); break;
     }
+    // ---- epilogue, staged through LDS so that the global stores are whole
+    //      128-byte lines (the MFMA layout gives a lane one token and 4
+    //      consecutive features: 8 bytes in each of 32 rows per store).  No
+    //      barrier: a wave stages only into its own 8 KB piece of the slots,
+    //      which only its own DMAs (all landed: it waited for them) fill, and
+    //      no wave reads the ring after the last K-step barrier.
     if (ntt == 0) return;
-
-    // ---- epilogue.  32x32 accumulator layout: lane holds token column
-    //      (lane & 31) and, for register r, weight row 8 (r / 4) + 4 lh + r % 4.
     const int bmine = bx + wt;
     const int toff = wt ? block_info(a.gs, a.gpo, a.gidx, bx + 1).token_offset : b0.token_offset;
+    // staged tile of this wave: 128 token rows x OB bytes (gate/up: 64
+    // features, down: 128), 16-byte chunks XOR-swizzled by row; RPP rows in
+    // each of the wave's 8 KB pieces (slot j: bytes j*SLOT + wave*8 KB ..)
+    constexpr int OB = DUAL ? 128 : 256;
+    constexpr int OC = OB / 16;  // chunks per row
+    constexpr int RPP = 8192 / OB;
+    static_assert(128 / RPP <= NWS + NTS, "staging fits in the wave's pieces");
+    auto stage_row = [&](int row) {
+        return smem + (row / RPP) * SLOT + wave * 8192 + (row % RPP) * OB;
+    };
+    // 32x32 accumulator layout: lane holds token column (lane & 31) and,
+    // for register 4q + r, weight row 8q + 4lh + r of its 32-row tile t
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int tok = 32 * u + lr;
-        if (tok >= myrows) continue;
-        const int64_t row = (int64_t)bmine * kBlockM + tok;
-        _Float16 *yrow = a.y + row * N + n0;
+        if (u >= ntt) continue;
+        const int row = 32 * u + lr;
+        unsigned char *srow = stage_row(row);
         if constexpr (DUAL) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -287,22 +301,36 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
                 for (int q = 0; q < 4; ++q) {
                     const f16x &g = acc[t][u];
                     const f16x &p = acc[t + 2][u];
-                    *(h4 *)(yrow + 64 * ww + 32 * t + 8 * q + 4 * lh) =
+                    const int c = (4 * t + q) ^ (row & (OC - 1));  // features 32t + 8q .. +7
+                    *(h4 *)(srow + (c << 4) + 8 * lh) =
                         to_h4(silu(g[4 * q + 0]) * p[4 * q + 0], silu(g[4 * q + 1]) * p[4 * q + 1],
                               silu(g[4 * q + 2]) * p[4 * q + 2], silu(g[4 * q + 3]) * p[4 * q + 3]);
                 }
             }
         } else {
-            const float w = a.rw[a.go[b0.e] + toff + tok];
+            const float w = row < myrows ? a.rw[a.go[b0.e] + toff + row] : 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f16x &o = acc[t][u];
-                    *(h4 *)(yrow + 128 * ww + 32 * t + 8 * q + 4 * lh) =
+                    const int c = (4 * t + q) ^ (row & (OC - 1));
+                    *(h4 *)(srow + (c << 4) + 8 * lh) =
                         to_h4(o[4 * q + 0] * w, o[4 * q + 1] * w, o[4 * q + 2] * w, o[4 * q + 3] * w);
                 }
             }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    // row-contiguous read-back: OC lanes per row, 64 / OC rows per instruction
+    _Float16 *ybase = a.y + (int64_t)bmine * kBlockM * N + n0 + (DUAL ? 64 : 128) * ww;
+    const int c = lane % OC;
+#pragma unroll 4
+    for (int r0 = 0; r0 < 32 * ntt; r0 += 64 / OC) {
+        const int row = r0 + lane / OC;
+        if (row < myrows) {
+            const h8 v = *(const h8 *)(stage_row(row) + ((c ^ (row & (OC - 1))) << 4));
+            *(h8 *)(ybase + (int64_t)row * N + 8 * c) = v;
         }
     }
 }
