@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     const BlockInfo b0 = block_info(a.gs, a.gpo, a.gidx, bx);
     const bool has1 = bx + 1 < last && bx + 1 < a.M;
     const int rows0 = b0.rows;
-    const int rows1 = has1 ? block_info(a.gs, a.gpo, a.gidx, bx + 1).rows : 0;
+    // block bx+1 belongs to the same expert: 128 rows further into its group
+    const int rows1 = has1 ? max(0, min(kBlockM, a.gs[e] - (b0.token_offset + kBlockM))) : 0;
     if (rows0 == 0 && rows1 == 0) return;
 
     const int64_t K = a.K, N = a.N;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     //      no wave reads the ring after the last K-step barrier.
     if (ntt == 0) return;
     const int bmine = bx + wt;
-    const int toff = wt ? block_info(a.gs, a.gpo, a.gidx, bx + 1).token_offset : b0.token_offset;
+    const int toff = b0.token_offset + kBlockM * wt;
     // staged tile of this wave: 128 token rows x OB bytes (gate/up: 64
     // features, down: 128), 16-byte chunks XOR-swizzled by row; RPP rows in
     // each of the wave's 8 KB pieces (slot j: bytes j*SLOT + wave*8 KB ..)
