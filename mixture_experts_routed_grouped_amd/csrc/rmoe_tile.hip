@@ -32,13 +32,14 @@
 // v_mfma_f32_32x32x16_f16 with weights as A (32 feature rows) and tokens as
 // B (32 token columns).  Token tiles beyond a block's valid rows are
 // skipped (the K loop is specialised on their count, a uniform value).
+#include <atomic>
 #include <type_traits>
 
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
 #ifndef RMOE_TILE_GROUP
-#define RMOE_TILE_GROUP 8   // weight slices per locality group (see tile_item)
+#define RMOE_TILE_GROUP 8   // weight slices per locality group (see tile_kernel)
 #endif
 
 namespace rmoe {
@@ -62,48 +63,19 @@ constexpr int SUB = BK / 16;                // MFMA sub-steps per K step
 // fill of step k+2, issued after the token fill of step k+1
 constexpr int VM_ALLOW = DMA_HALF;
 
-// Work item of workgroup w in an order that keeps operand sharing inside one
-// XCD's L2.  Items (weight slice nt, block bx) are listed group by group:
-// a group is RMOE_TILE_GROUP consecutive slices, and within a group blocks
-// run in order with the group's slices innermost.  Blocks of one expert are
-// consecutive, so the workgroups an XCD runs at the same time cover a few
-// slices of the same expert's weights and a few token blocks.  The list is
-// cut into 8 contiguous parts, one per XCD (workgroup w runs on XCD w % 8).
-// Returns false for padding workgroups.
-__device__ __forceinline__ bool tile_item(int w, int NT, int M, int &nt, int &bx) {
-    const int total = NT * M;
-    const int per = (total + kXcd - 1) / kXcd;
-    const int item = (w % kXcd) * per + w / kXcd;
-    if (w / kXcd >= per || item >= total) return false;
-    const int gsz = RMOE_TILE_GROUP * M;
-    const int g = item / gsz, r = item - g * gsz;
-    const int width = min(RMOE_TILE_GROUP, NT - g * RMOE_TILE_GROUP);
-    bx = r / width;
-    nt = g * RMOE_TILE_GROUP + (r - bx * width);
-    return true;
-}
-
-// grid: ceil(NT * M / 8) * 8 workgroups of 256 threads; NT = N / 128 slices
-// for gate/up and ceil(N / 256) for down.  Dynamic LDS: LDS_BYTES.
+// One tile: blocks bx (b0: its expert, offset in the group, valid rows) and
+// bx+1 (rows1 valid rows; has1: it belongs to the same expert) against the
+// weight slice nt.  Called with the workgroup's LDS; leaves no DMA in flight.
 template <bool DUAL>
-__global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
-    int nt, bx;
-    if (!tile_item(blockIdx.x, NT, a.M, nt, bx)) return;
-    // block pairs: the first block of an expert and every second one after it
-    const int e = a.gidx[bx];
-    const int first = a.gpo[e] / kBlockM, last = a.gpo[e + 1] / kBlockM;  // [first, last)
-    if ((bx - first) & 1) return;
-    const BlockInfo b0 = block_info(a.gs, a.gpo, a.gidx, bx);
-    const bool has1 = bx + 1 < last && bx + 1 < a.M;
+__device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem, int nt, int bx,
+                                         const BlockInfo &b0, bool has1, int rows1) {
     const int rows0 = b0.rows;
-    // block bx+1 belongs to the same expert: 128 rows further into its group
-    const int rows1 = has1 ? max(0, min(kBlockM, a.gs[e] - (b0.token_offset + kBlockM))) : 0;
-    if (rows0 == 0 && rows1 == 0) return;
-
     const int64_t K = a.K, N = a.N;
-    const int tid = threadIdx.x;
+    // opaque per tile: keeps the compiler from hoisting per-lane address
+    // arithmetic out of a loop over tiles, where it would stay live (and
+    // spill) through the K loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
@@ -336,18 +308,77 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     }
 }
 
-unsigned tile_grid(int NT, int M) {
-    const long total = (long)NT * M;
-    return (unsigned)(((total + kXcd - 1) / kXcd) * kXcd);
+// Persistent kernel: one workgroup per CU (a multiple of 8 of them, LDS_BYTES
+// of dynamic LDS each), looping over work items, all live: a pair of blocks
+// of one expert that holds valid rows, times a weight slice (NT = N / 128
+// slices for gate/up, ceil(N / 256) for down).  Items are listed slice group
+// by slice group (RMOE_TILE_GROUP slices), pairs in expert order within a
+// group, the group's slices innermost; the list is cut into 8 contiguous
+// parts, one per XCD (workgroup w runs on XCD w % 8), so the 32 workgroups
+// of an XCD run a rectangle of 4 consecutive pairs x 8 slices at a time --
+// operands they share in that XCD's L2.
+template <bool DUAL>
+__global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // live pairs of expert e: its blocks with valid rows, two per pair
+    auto pairs_of = [&](int e) { return ((a.gs[e] + kBlockM - 1) / kBlockM + 1) / 2; };
+    int P = 0;
+    for (int e = 0; e < a.E; ++e) P += pairs_of(e);
+    const int total = P * NT;
+    const int per = (total + kXcd - 1) / kXcd;
+    const int xcd = blockIdx.x % kXcd, lane_of_xcd = blockIdx.x / kXcd, nl = gridDim.x / kXcd;
+    const int end = min(total, (xcd + 1) * per);
+    int ce = 0, cp0 = 0;  // cursor: an expert and the index of its first pair
+    for (int item = xcd * per + lane_of_xcd; item < end; item += nl) {
+        const int gsz = RMOE_TILE_GROUP * P;
+        const int g = item / gsz, r = item - g * gsz;
+        const int width = min(RMOE_TILE_GROUP, NT - g * RMOE_TILE_GROUP);
+        const int p = r / width;
+        const int nt = g * RMOE_TILE_GROUP + (r - p * width);
+        if (p < cp0) ce = cp0 = 0;  // a new slice group starts the pairs again
+        while (p >= cp0 + pairs_of(ce)) {
+            cp0 += pairs_of(ce);
+            ++ce;
+        }
+        const int q = p - cp0, gse = a.gs[ce];
+        BlockInfo b0;
+        b0.e = ce;
+        b0.token_offset = 2 * kBlockM * q;
+        b0.rows = min(kBlockM, gse - b0.token_offset);
+        const int rows1 = max(0, min(kBlockM, gse - b0.token_offset - kBlockM));
+        run_tile<DUAL>(a, smem, nt, a.gpo[ce] / kBlockM + 2 * q, b0, rows1 > 0, rows1);
+    }
+}
+
+// Workgroup slots of the persistent kernel on the current device: its CU
+// count rounded down to a multiple of 8 (cached per device).
+hipError_t persistent_grid(unsigned &grid) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int n = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        n = n / kXcd * kXcd;
+        if (n < kXcd) n = kXcd;
+        if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    }
+    grid = (unsigned)n;
+    return hipSuccess;
 }
 
 template <bool DUAL>
 hipError_t launch(const StageArgs &a, int NT, hipStream_t s) {
-    const unsigned lds = LDS_BYTES;  // above the 64 KB default, so opt in
-    hipError_t e = hipFuncSetAttribute((const void *)tile_kernel<DUAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    unsigned grid = 0;
+    hipError_t e = persistent_grid(grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(tile_kernel<DUAL>, dim3(tile_grid(NT, a.M)), dim3(256), lds, s, a, NT);
+    const unsigned lds = LDS_BYTES;  // above the 64 KB default, so opt in
+    e = hipFuncSetAttribute((const void *)tile_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tile_kernel<DUAL>, dim3(grid), dim3(256), lds, s, a, NT);
     return hipGetLastError();
 }
 
