@@ -85,6 +85,8 @@ def test_tiny(variant):
     (2, 3, 3, 200, 384, 256, "uniform"),   # H % 256 == 128: half-width last down slice
     (3, 8, 2, 37, 512, 128, "uniform"),    # tiny groups, empty-ish experts
     (4, 2, 1, 520, 128, 640, "uniform"),   # four full blocks per expert, long I
+    (5, 40, 4, 3000, 512, 1024, "zipf"),   # more tiles than workgroup slots: each loops
+    (6, 12, 2, 2000, 256, 2304, "uniform"),  # 18 gate/up slices: groups of 8, 8, 2
 ])
 def test_random_shapes(variant, seed, E, k, T, H, I, routing):
     cfg = workloads.Config(f"r{seed}", T, E, k, H, I, routing=routing, zipf_s=1.4, seed=seed)
