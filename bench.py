@@ -104,7 +104,8 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
     the headline scope): the router (synthetic gate [E, H]), the device-side
     contract build from device top-k ids, the pack, the combine, and the
     whole layer -- router, device contract, pack, both expert kernels,
-    combine -- with no host round trip."""
+    combine -- with no host round trip; for the tiled family also the
+    single-launch forward beside the two-launch one."""
     import torch
     import mixture_experts_routed_grouped_amd as R
     import workloads
@@ -138,6 +139,15 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
         "combine": lambda: R.combine(out, d["padded_row_of_pair"], cfg.top_k, y),
         "layer_e2e": layer,
     }
+    if variant == "tile":
+        # both tiled stages in one launch, against the two launches, on the
+        # same device tables (tiled family only: prefill-shaped batches)
+        sync = R.fused_sync(dev, d["num_blocks_m"])
+        tables = (d["group_sizes"], d["group_offsets"], d["group_padded_offsets"], d["group_idx_for_bx"])
+        steps["forward_two_launch"] = lambda: R.forward(stacked, inp.wg, inp.wu, inp.wd, w_compact,
+                                                        *tables, hid, out, variant="tile")
+        steps["forward_fused"] = lambda: R.forward_fused(stacked, inp.wg, inp.wu, inp.wd, w_compact,
+                                                         *tables, hid, out, sync=sync)
     res = {}
     for name, fn in steps.items():
         for _ in range(3):

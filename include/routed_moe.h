@@ -146,6 +146,45 @@ RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const v
                                       int32_t variant, void *stream);
 
 /*
+ * Both stages in ONE launch ("MetaX-TileLang工具链", section 1.12.4: the
+ * hidden intermediate's global write and re-read, and kernel fusion as the
+ * way to cut it).  Same arguments, layouts and results as
+ * rmoe_forward_f16_variant with RMOE_VARIANT_TILE, on any shape; meant for
+ * prefill-shaped batches.  One persistent kernel runs every gate/up tile,
+ * then every down tile; a down tile starts as soon as all gate/up tiles of
+ * its own pair of blocks have published their hidden rows, so the two
+ * stages overlap at the hand-over and the hidden rows are re-read while they
+ * are still in the caches (the workspace is still written: it is the
+ * hand-over buffer, not a second output).
+ *   sync: int32 device scratch of rmoe_fused_sync_words(num_blocks_m) words,
+ *         caller-owned.  It must be all zero before its first use; every
+ *         call that runs to completion leaves it zero again, except
+ *         sync[RMOE_FUSED_SYNC_ERROR], a sticky count of tiles skipped
+ *         because a wait for hidden rows timed out (2 s; then every later
+ *         wait of that launch gives up at once, so the call still ends).
+ *         It is 0 in normal operation; non-zero means out is incomplete.  Calls that share one sync buffer
+ *         must not overlap in time (use one stream, or one buffer each).
+ * Returns as rmoe_forward_f16; the launch is asynchronous, nothing is read
+ * back.
+ */
+#define RMOE_FUSED_SYNC_TICKETS 0 /* [8] one work queue per locality group */
+#define RMOE_FUSED_SYNC_EXIT 8    /* workgroups done */
+#define RMOE_FUSED_SYNC_ERROR 9   /* sticky: skipped tiles */
+#define RMOE_FUSED_SYNC_ABORT 10  /* this launch gave up waiting (reset on exit) */
+#define RMOE_FUSED_SYNC_HEAD 16   /* then [num_blocks_m]: gate/up tiles done per pair */
+RMOE_API size_t rmoe_fused_sync_words(int32_t num_blocks_m);
+RMOE_API int rmoe_forward_fused_f16(const void *stacked_expert_tokens, const void *gate_w,
+                                    const void *up_w, const void *down_w,
+                                    const float *routed_expert_weights,
+                                    const int32_t *group_sizes, const int32_t *group_offsets,
+                                    const int32_t *group_padded_offsets,
+                                    const int32_t *group_idx_for_bx, void *workspace, void *out,
+                                    int32_t *sync, int64_t hidden, int64_t intermediate,
+                                    int32_t num_experts, int64_t total_padded_tokens,
+                                    int64_t total_valid_tokens, int32_t num_blocks_m,
+                                    void *stream);
+
+/*
  * Stage 1 alone (the Step-1 grid of section 完整算子代码): workspace rows =
  * fp16(silu(x.Wg^T) * (x.Wu^T)) for valid rows.  Arguments as above.
  */

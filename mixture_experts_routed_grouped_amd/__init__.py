@@ -45,6 +45,8 @@ _SIGS = {
     "rmoe_forward_f16": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
     "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
                                  ctypes.c_int),
+    "rmoe_fused_sync_words": ([_I32], ctypes.c_size_t),
+    "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
     "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
@@ -195,6 +197,64 @@ def forward(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, 
         _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
         _dev(out, f16, "out"), H, I, E, Tp, pairs, M, _VARIANTS[variant], _stream(x, stream))
     _check(st, "rmoe_forward_f16")
+
+
+FUSED_SYNC_ERROR = 9  # RMOE_FUSED_SYNC_ERROR: sticky count of skipped tiles
+_SYNC = {}
+
+
+def fused_sync_words(num_blocks_m: int) -> int:
+    return int(lib().rmoe_fused_sync_words(int(num_blocks_m)))
+
+
+def fused_sync(device, num_blocks_m: int):
+    """A zeroed int32 sync buffer for forward_fused, cached per (device,
+    size); the kernel leaves it zero after each completed call."""
+    torch = _torch()
+    device = torch.device(device)
+    key = (device.index or 0, fused_sync_words(num_blocks_m))
+    buf = _SYNC.get(key)
+    if buf is None:
+        buf = torch.zeros(key[1], dtype=torch.int32, device=device)
+        _SYNC[key] = buf
+    return buf
+
+
+def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
+                  group_offsets, group_padded_offsets, group_idx_for_bx, workspace, out, sync=None,
+                  stream=None):
+    """Both stages in one launch (rmoe_forward_fused_f16): same arguments and
+    results as forward(..., variant="tile"); ``sync`` is the int32 queue
+    state (default: a cached zeroed buffer; calls sharing one must not
+    overlap in time)."""
+    torch = _torch()
+    x = stacked_expert_tokens
+    E, I, H = gate_w.shape
+    Tp = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != H or tuple(up_w.shape) != (E, I, H) or \
+            tuple(down_w.shape) != (E, H, I):
+        raise ValueError("inconsistent shapes")
+    if tuple(workspace.shape) != (Tp, I) or tuple(out.shape) != (Tp, H):
+        raise ValueError("workspace must be [Tp, I] and out [Tp, H]")
+    if group_sizes.numel() != E or group_offsets.numel() != E + 1 or \
+            group_padded_offsets.numel() != E + 1:
+        raise ValueError("group tables must have E, E+1, E+1 entries")
+    M = group_idx_for_bx.numel()
+    if sync is None:
+        sync = fused_sync(x.device, M)
+    if sync.numel() < fused_sync_words(M):
+        raise ValueError("sync buffer too small")
+    f16, i32 = torch.float16, torch.int32
+    st = lib().rmoe_forward_fused_f16(
+        _dev(x, f16, "stacked_expert_tokens"), _dev(gate_w, f16, "gate_w"),
+        _dev(up_w, f16, "up_w"), _dev(down_w, f16, "down_w"),
+        _dev(routed_expert_weights, torch.float32, "routed_expert_weights"),
+        _dev(group_sizes, i32, "group_sizes"), _dev(group_offsets, i32, "group_offsets"),
+        _dev(group_padded_offsets, i32, "group_padded_offsets"),
+        _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
+        _dev(out, f16, "out"), _dev(sync, i32, "sync"), H, I, E, Tp,
+        routed_expert_weights.numel(), M, _stream(x, stream))
+    _check(st, "rmoe_forward_fused_f16")
 
 
 def gate_up(stacked_expert_tokens, gate_w, up_w, group_sizes, group_padded_offsets,

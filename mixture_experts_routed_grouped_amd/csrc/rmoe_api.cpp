@@ -16,7 +16,10 @@ constexpr int64_t B = RMOE_BLOCK_M;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-constexpr int32_t kMaxDeviceExperts = 8192;  // the device contract keeps per-expert tables in LDS
+constexpr int32_t kMaxDeviceExperts = 8192;
+// how long a fused down tile waits for its pair's hidden rows before it gives
+// up (the longest real wait is one gate/up stage: milliseconds)
+constexpr int kFusedWaitMs = 2000;  // the device contract keeps per-expert tables in LDS
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -266,6 +269,52 @@ int rmoe_forward_f16(const void *x, const void *gate_w, const void *up_w, const 
     return rmoe_forward_f16_variant(x, gate_w, up_w, down_w, rw, gs, go, gpo, gidx, workspace,
                                     out, hidden, intermediate, num_experts, total_padded_tokens,
                                     total_valid_tokens, num_blocks_m, RMOE_VARIANT_AUTO, stream);
+}
+
+size_t rmoe_fused_sync_words(int32_t num_blocks_m) {
+    return num_blocks_m < 0 ? 0 : (size_t)RMOE_FUSED_SYNC_HEAD + (size_t)num_blocks_m;
+}
+
+int rmoe_forward_fused_f16(const void *x, const void *gate_w, const void *up_w,
+                           const void *down_w, const float *rw, const int32_t *gs,
+                           const int32_t *go, const int32_t *gpo, const int32_t *gidx,
+                           void *workspace, void *out, int32_t *sync, int64_t hidden,
+                           int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
+                           int64_t total_valid_tokens, int32_t num_blocks_m, void *stream) {
+    int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
+    if (st != RMOE_OK) return st;
+    if (total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!x || !gate_w || !up_w || !down_w || !gs || !go || !gpo || !workspace || !out || !sync ||
+        (num_blocks_m > 0 && !gidx) || (total_valid_tokens > 0 && !rw))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(gate_w) || !aligned16(up_w) || !aligned16(down_w) ||
+        !aligned16(workspace) || !aligned16(out) || !aligned4(rw) || !aligned4(gs) ||
+        !aligned4(go) || !aligned4(gpo) || !aligned4(gidx) || !aligned4(sync))
+        return RMOE_ERR_MISALIGNED;
+    if (num_blocks_m == 0) return RMOE_OK;
+    rmoe::StageArgs gu{}, dn{};
+    gu.x = static_cast<const _Float16 *>(x);
+    gu.w0 = static_cast<const _Float16 *>(gate_w);
+    gu.w1 = static_cast<const _Float16 *>(up_w);
+    gu.y = static_cast<_Float16 *>(workspace);
+    gu.K = hidden;
+    gu.N = intermediate;
+    dn.x = static_cast<const _Float16 *>(workspace);
+    dn.w0 = static_cast<const _Float16 *>(down_w);
+    dn.rw = rw;
+    dn.y = static_cast<_Float16 *>(out);
+    dn.K = intermediate;
+    dn.N = hidden;
+    for (rmoe::StageArgs *a : {&gu, &dn}) {
+        a->gs = gs;
+        a->go = go;
+        a->gpo = gpo;
+        a->gidx = gidx;
+        a->E = num_experts;
+        a->M = num_blocks_m;
+        a->pairs = total_valid_tokens;
+    }
+    return to_status(rmoe::launch_fused(gu, dn, sync, kFusedWaitMs, static_cast<hipStream_t>(stream)));
 }
 
 int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,

@@ -35,6 +35,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "../../include/routed_moe.h"
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
@@ -62,11 +63,16 @@ constexpr int SUB = BK / 16;                // MFMA sub-steps per K step
 // vmcnt a wave may leave outstanding when it publishes step k+1: the weight
 // fill of step k+2, issued after the token fill of step k+1
 constexpr int VM_ALLOW = DMA_HALF;
+constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc1 (device scope)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // One tile: blocks bx (b0: its expert, offset in the group, valid rows) and
 // bx+1 (rows1 valid rows; has1: it belongs to the same expert) against the
 // weight slice nt.  Called with the workgroup's LDS; leaves no DMA in flight.
-template <bool DUAL>
+// WT: store the output tile write-through at device scope (sc1), so that a
+// store that has completed (vmcnt) is visible to every XCD without an L2
+// write-back; the single-launch path hands the hidden rows over this way.
+template <bool DUAL, bool WT = false>
 __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem, int nt, int bx,
                                          const BlockInfo &b0, bool has1, int rows1) {
     const int rows0 = b0.rows;
@@ -298,55 +304,184 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
     // row-contiguous read-back: OC lanes per row, 64 / OC rows per instruction
     _Float16 *ybase = a.y + (int64_t)bmine * kBlockM * N + n0 + (DUAL ? 64 : 128) * ww;
     const int c = lane % OC;
+    // buffer view of this wave's output tile (128 rows of N, < 2^31 bytes)
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t yres =
+        __builtin_amdgcn_make_buffer_rsrc(ybase, 0, 0x7fffffff, 0x00020000);
 #pragma unroll 4
     for (int r0 = 0; r0 < 32 * ntt; r0 += 64 / OC) {
         const int row = r0 + lane / OC;
         if (row < myrows) {
             const h8 v = *(const h8 *)(stage_row(row) + ((c ^ (row & (OC - 1))) << 4));
-            *(h8 *)(ybase + (int64_t)row * N + 8 * c) = v;
+            if constexpr (WT)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), yres,
+                                                       (int)(((int64_t)row * N + 8 * c) * 2), 0,
+                                                       kCpolSc1);
+            else
+                *(h8 *)(ybase + (int64_t)row * N + 8 * c) = v;
         }
     }
+}
+
+// Live pairs of expert e: its blocks with valid rows, two per pair.
+__device__ __forceinline__ int pairs_of(const StageArgs &a, int e) {
+    return ((a.gs[e] + kBlockM - 1) / kBlockM + 1) / 2;
+}
+
+// Work item -> (weight slice, pair).  Items are listed slice group by slice
+// group (RMOE_TILE_GROUP slices), pairs in expert order within a group, the
+// group's slices innermost.  (ce, cp0) is a cursor -- an expert and the index
+// of its first pair -- that only moves forward while the items do.
+struct ItemPos {
+    int nt, bx, rows1;
+    BlockInfo b0;
+};
+__device__ __forceinline__ ItemPos decode_item(const StageArgs &a, int P, int NT, int item, int &ce,
+                                               int &cp0) {
+    const int gsz = RMOE_TILE_GROUP * P;
+    const int g = item / gsz, r = item - g * gsz;
+    const int width = min(RMOE_TILE_GROUP, NT - g * RMOE_TILE_GROUP);
+    const int p = r / width;
+    ItemPos it;
+    it.nt = g * RMOE_TILE_GROUP + (r - p * width);
+    if (p < cp0) ce = cp0 = 0;  // a new slice group starts the pairs again
+    while (p >= cp0 + pairs_of(a, ce)) {
+        cp0 += pairs_of(a, ce);
+        ++ce;
+    }
+    const int q = p - cp0, gse = a.gs[ce];
+    it.b0.e = ce;
+    it.b0.token_offset = 2 * kBlockM * q;
+    it.b0.rows = min(kBlockM, gse - it.b0.token_offset);
+    it.rows1 = max(0, min(kBlockM, gse - it.b0.token_offset - kBlockM));
+    it.bx = a.gpo[ce] / kBlockM + 2 * q;
+    return it;
 }
 
 // Persistent kernel: one workgroup per CU (a multiple of 8 of them, LDS_BYTES
 // of dynamic LDS each), looping over work items, all live: a pair of blocks
 // of one expert that holds valid rows, times a weight slice (NT = N / 128
-// slices for gate/up, ceil(N / 256) for down).  Items are listed slice group
-// by slice group (RMOE_TILE_GROUP slices), pairs in expert order within a
-// group, the group's slices innermost; the list is cut into 8 contiguous
-// parts, one per XCD (workgroup w runs on XCD w % 8), so the 32 workgroups
-// of an XCD run a rectangle of 4 consecutive pairs x 8 slices at a time --
-// operands they share in that XCD's L2.
+// slices for gate/up, ceil(N / 256) for down).  The item list is cut into 8
+// contiguous parts, one per XCD (workgroup w runs on XCD w % 8), so the 32
+// workgroups of an XCD run a rectangle of 4 consecutive pairs x 8 slices at
+// a time -- operands they share in that XCD's L2.
 template <bool DUAL>
 __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    // live pairs of expert e: its blocks with valid rows, two per pair
-    auto pairs_of = [&](int e) { return ((a.gs[e] + kBlockM - 1) / kBlockM + 1) / 2; };
     int P = 0;
-    for (int e = 0; e < a.E; ++e) P += pairs_of(e);
+    for (int e = 0; e < a.E; ++e) P += pairs_of(a, e);
     const int total = P * NT;
     const int per = (total + kXcd - 1) / kXcd;
     const int xcd = blockIdx.x % kXcd, lane_of_xcd = blockIdx.x / kXcd, nl = gridDim.x / kXcd;
     const int end = min(total, (xcd + 1) * per);
-    int ce = 0, cp0 = 0;  // cursor: an expert and the index of its first pair
+    int ce = 0, cp0 = 0;
     for (int item = xcd * per + lane_of_xcd; item < end; item += nl) {
-        const int gsz = RMOE_TILE_GROUP * P;
-        const int g = item / gsz, r = item - g * gsz;
-        const int width = min(RMOE_TILE_GROUP, NT - g * RMOE_TILE_GROUP);
-        const int p = r / width;
-        const int nt = g * RMOE_TILE_GROUP + (r - p * width);
-        if (p < cp0) ce = cp0 = 0;  // a new slice group starts the pairs again
-        while (p >= cp0 + pairs_of(ce)) {
-            cp0 += pairs_of(ce);
-            ++ce;
+        const ItemPos it = decode_item(a, P, NT, item, ce, cp0);
+        run_tile<DUAL>(a, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
+    }
+}
+
+// ---- Both stages in one launch.
+//
+// The same tiles as the two persistent launches, taken from one queue per
+// locality group (workgroup w serves group w % 8, i.e. its XCD): first the
+// group's gate/up items, then its down items, in the orders above.  A down
+// item of the pair at block bx needs every gate/up slice of that pair in the
+// hidden workspace, so gate/up items count themselves into done[bx] once
+// their stores are out, and a down item waits until done[bx] reaches the
+// slice count.  The XCDs' L2 caches are not coherent with each other: the
+// gate/up tiles of this launch store their hidden rows with device-scope
+// (sc1) write-through stores and wait for them to complete before counting
+// -- the effect of an agent-scope release without writing back the whole L2,
+// which measured ~2-5% of the launch -- and a down tile drops its CU's and
+// XCD's stale copies (agent-scope acquire) before reading them.
+// Progress: a workgroup waits only while holding a down ticket, i.e. after
+// every gate/up ticket of its own queue was handed to a running workgroup,
+// and gate/up items never wait; so every wait ends once one workgroup of each
+// queue runs.  Each wait is bounded all the same, by wait_ticks of the
+// constant-rate real-time counter: a wait that gives up skips its item, adds
+// 1 to the sticky error word and raises the launch's abort flag, after which
+// every wait gives up at once, so the kernel always exits within about one
+// deadline.  The last workgroup out returns the tickets, the counters, the
+// abort flag and the exit count to zero, ready for the next launch.
+__global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, int32_t *sync,
+                                                    uint64_t wait_ticks) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int *bcast = reinterpret_cast<int *>(smem);  // LDS is idle between items
+    int32_t *tickets = sync + RMOE_FUSED_SYNC_TICKETS;
+    int32_t *done = sync + RMOE_FUSED_SYNC_HEAD;
+    const int NT1 = (int)(gu.N / 128), NT2 = (int)((dn.N + 255) / 256);
+    int P = 0;
+    for (int e = 0; e < gu.E; ++e) P += pairs_of(gu, e);
+    const int grp = blockIdx.x % kXcd;
+    const int total1 = P * NT1, total2 = P * NT2;
+    const int per1 = (total1 + kXcd - 1) / kXcd, per2 = (total2 + kXcd - 1) / kXcd;
+    const int lo1 = grp * per1, lo2 = grp * per2;
+    const int n1 = max(0, min(total1, lo1 + per1) - lo1), n2 = max(0, min(total2, lo2 + per2) - lo2);
+    int ce = 0, cp0 = 0;
+    for (;;) {
+        __syncthreads();  // every wave is done with the LDS of the last item
+        if (threadIdx.x == 0)
+            bcast[0] = __hip_atomic_fetch_add(tickets + grp, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int t = bcast[0];
+        if (t >= n1 + n2) break;
+        if (t < n1) {
+            const ItemPos it = decode_item(gu, P, NT1, lo1 + t, ce, cp0);
+            __syncthreads();  // the ticket is read before the DMAs reuse its LDS word
+            run_tile<true, true>(gu, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
+            // the hidden rows went out write-through at device scope; once
+            // every wave's stores have completed they are visible to all
+            // XCDs, and the count may go up (no L2 write-back needed)
+            wait_vm<0>();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(done + it.bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const ItemPos it = decode_item(dn, P, NT2, lo2 + (t - n1), ce, cp0);
+            if (threadIdx.x == 0) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                bool ready;
+                for (;;) {
+                    ready = __hip_atomic_load(done + it.bx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NT1;
+                    if (ready) break;
+                    // give up past the deadline, or at once once any wait of this launch has
+                    if (__hip_atomic_load(sync + RMOE_FUSED_SYNC_ABORT, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+                        __builtin_amdgcn_s_memrealtime() - t0 > wait_ticks)
+                        break;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                // acquire: drop this CU's and XCD's stale copies before any wave reads
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if (!ready) {
+                    __hip_atomic_fetch_add(sync + RMOE_FUSED_SYNC_ERROR, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(sync + RMOE_FUSED_SYNC_ABORT, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                bcast[1] = ready;
+            }
+            __syncthreads();
+            const bool ready = bcast[1] != 0;
+            __syncthreads();  // the flag is read before the DMAs reuse its LDS word
+            if (!ready) continue;
+            run_tile<false>(dn, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
         }
-        const int q = p - cp0, gse = a.gs[ce];
-        BlockInfo b0;
-        b0.e = ce;
-        b0.token_offset = 2 * kBlockM * q;
-        b0.rows = min(kBlockM, gse - b0.token_offset);
-        const int rows1 = max(0, min(kBlockM, gse - b0.token_offset - kBlockM));
-        run_tile<DUAL>(a, smem, nt, a.gpo[ce] / kBlockM + 2 * q, b0, rows1 > 0, rows1);
+    }
+    // the last workgroup out resets the queue state (the error word stays)
+    __syncthreads();  // every wave has read the final ticket
+    if (threadIdx.x == 0)
+        bcast[0] = __hip_atomic_fetch_add(sync + RMOE_FUSED_SYNC_EXIT, 1, __ATOMIC_ACQ_REL,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (bcast[0]) {
+        for (int i = threadIdx.x; i < kXcd; i += blockDim.x) tickets[i] = 0;
+        for (int i = threadIdx.x; i < gu.M; i += blockDim.x) done[i] = 0;
+        if (threadIdx.x == 0) {
+            sync[RMOE_FUSED_SYNC_ABORT] = 0;
+            sync[RMOE_FUSED_SYNC_EXIT] = 0;
+        }
     }
 }
 
@@ -390,6 +525,25 @@ hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s) {
 
 hipError_t launch_tile_down(const StageArgs &a, hipStream_t s) {
     return launch<false>(a, (int)((a.N + 255) / 256), s);
+}
+
+hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int wait_ms,
+                        hipStream_t s) {
+    unsigned grid = 0;
+    hipError_t e = persistent_grid(grid);
+    if (e != hipSuccess) return e;
+    int dev = 0, khz = 0;  // real-time counter rate
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return e;
+    if (khz <= 0) khz = 100000;
+    const unsigned lds = LDS_BYTES;
+    e = hipFuncSetAttribute((const void *)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fused_kernel, dim3(grid), dim3(256), lds, s, gu, dn, sync,
+                       (uint64_t)khz * (uint64_t)wait_ms);
+    return hipGetLastError();
 }
 
 }  // namespace rmoe

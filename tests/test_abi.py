@@ -182,3 +182,22 @@ def test_router_argument_errors_without_gpu():
     assert rt(x=odd) == -3
     assert rt(T=0, x=None) == 0                           # nothing to do
     assert rt(k=0, ids=None) == 0
+
+
+def test_fused_argument_errors_without_gpu():
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10002)
+
+    def fz(H=256, I=128, E=4, Tp=640, pairs=18, M=5, sync=fake, x=fake):
+        return L.rmoe_forward_fused_f16(x, *([fake] * 10), sync, H, I, E, Tp, pairs, M, None)
+
+    assert L.rmoe_fused_sync_words(5) == 16 + 5
+    assert L.rmoe_fused_sync_words(-1) == 0
+    assert fz(sync=None) == -1                            # the queue state is required
+    assert fz(H=200) == -2
+    assert fz(Tp=512) == -1
+    assert fz(pairs=-1) == -1
+    assert fz(x=odd) == -3
+    assert fz(sync=ctypes.c_void_p(0x10002)) == -3        # int32 words
+    assert fz(M=0, Tp=0, pairs=0) == 0                    # no blocks: nothing launched
