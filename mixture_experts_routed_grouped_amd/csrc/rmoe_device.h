@@ -68,6 +68,14 @@ __device__ __forceinline__ void dma16(const void *g, unsigned lds) {
                  : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for lines read once (streamed weight
+// rows): MI355X serves a read stream with that hint ~13% faster (about 7.0
+// against 6.2 TB/s in a 4 GiB read probe).
+__device__ __forceinline__ void dma16_nt(const void *g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(g)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their no-wait maxima).
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -110,8 +110,14 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
 #pragma unroll
         for (int m = 0; m <= NM; ++m)
 #pragma unroll
-            for (int j = 0; j < (m == NM ? TD : 4); ++j)
-                dma16(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
+            for (int j = 0; j < (m == NM ? TD : 4); ++j) {
+                // weight rows are read once: non-temporal; token rows are
+                // shared by every slice of the block: cached normally
+                if (m == NM)
+                    dma16(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
+                else
+                    dma16_nt(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
+            }
     };
 
     f16x acc[NM];
