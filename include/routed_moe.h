@@ -160,9 +160,12 @@ RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const v
  *         caller-owned.  It must be all zero before its first use; every
  *         call that runs to completion leaves it zero again, except
  *         sync[RMOE_FUSED_SYNC_ERROR], a sticky count of tiles skipped
- *         because a wait for hidden rows timed out (2 s; then every later
- *         wait of that launch gives up at once, so the call still ends).
- *         It is 0 in normal operation; non-zero means out is incomplete.  Calls that share one sync buffer
+ *         because a wait for hidden rows timed out (then every later wait
+ *         of that launch gives up at once, so the call still ends).  It is
+ *         0 in normal operation; non-zero means out is incomplete.
+ *   max_wait_us: how long a down tile may wait for its pair's hidden rows;
+ *         <= 0 selects the default, 2 s (real waits last at most one
+ *         gate/up stage, i.e. milliseconds).  Calls that share one sync buffer
  *         must not overlap in time (use one stream, or one buffer each).
  * Returns as rmoe_forward_f16; the launch is asynchronous, nothing is read
  * back.
@@ -182,7 +185,7 @@ RMOE_API int rmoe_forward_fused_f16(const void *stacked_expert_tokens, const voi
                                     int32_t *sync, int64_t hidden, int64_t intermediate,
                                     int32_t num_experts, int64_t total_padded_tokens,
                                     int64_t total_valid_tokens, int32_t num_blocks_m,
-                                    void *stream);
+                                    int32_t max_wait_us, void *stream);
 
 /*
  * Stage 1 alone (the Step-1 grid of section 完整算子代码): workspace rows =

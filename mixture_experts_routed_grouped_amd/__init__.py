@@ -46,7 +46,7 @@ _SIGS = {
     "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
                                  ctypes.c_int),
     "rmoe_fused_sync_words": ([_I32], ctypes.c_size_t),
-    "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
+    "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
@@ -222,11 +222,12 @@ def fused_sync(device, num_blocks_m: int):
 
 def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
                   group_offsets, group_padded_offsets, group_idx_for_bx, workspace, out, sync=None,
-                  stream=None):
+                  max_wait_us=0, stream=None):
     """Both stages in one launch (rmoe_forward_fused_f16): same arguments and
     results as forward(..., variant="tile"); ``sync`` is the int32 queue
     state (default: a cached zeroed buffer; calls sharing one must not
-    overlap in time)."""
+    overlap in time); ``max_wait_us`` bounds a down tile's wait for its
+    hidden rows (0: the library's default)."""
     torch = _torch()
     x = stacked_expert_tokens
     E, I, H = gate_w.shape
@@ -253,7 +254,7 @@ def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_wei
         _dev(group_padded_offsets, i32, "group_padded_offsets"),
         _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
         _dev(out, f16, "out"), _dev(sync, i32, "sync"), H, I, E, Tp,
-        routed_expert_weights.numel(), M, _stream(x, stream))
+        routed_expert_weights.numel(), M, int(max_wait_us), _stream(x, stream))
     _check(st, "rmoe_forward_fused_f16")
 
 

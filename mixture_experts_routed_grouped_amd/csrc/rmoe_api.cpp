@@ -17,9 +17,9 @@ constexpr int64_t B = RMOE_BLOCK_M;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 constexpr int32_t kMaxDeviceExperts = 8192;
-// how long a fused down tile waits for its pair's hidden rows before it gives
-// up (the longest real wait is one gate/up stage: milliseconds)
-constexpr int kFusedWaitMs = 2000;  // the device contract keeps per-expert tables in LDS
+// default bound on how long a fused down tile waits for its pair's hidden
+// rows (the longest real wait is one gate/up stage: milliseconds)
+constexpr int64_t kFusedWaitUs = 2000000;  // the device contract keeps per-expert tables in LDS
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -280,7 +280,8 @@ int rmoe_forward_fused_f16(const void *x, const void *gate_w, const void *up_w,
                            const int32_t *go, const int32_t *gpo, const int32_t *gidx,
                            void *workspace, void *out, int32_t *sync, int64_t hidden,
                            int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
-                           int64_t total_valid_tokens, int32_t num_blocks_m, void *stream) {
+                           int64_t total_valid_tokens, int32_t num_blocks_m, int32_t max_wait_us,
+                           void *stream) {
     int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
     if (st != RMOE_OK) return st;
     if (total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
@@ -314,7 +315,8 @@ int rmoe_forward_fused_f16(const void *x, const void *gate_w, const void *up_w,
         a->M = num_blocks_m;
         a->pairs = total_valid_tokens;
     }
-    return to_status(rmoe::launch_fused(gu, dn, sync, kFusedWaitMs, static_cast<hipStream_t>(stream)));
+    const int64_t wait_us = max_wait_us > 0 ? max_wait_us : kFusedWaitUs;
+    return to_status(rmoe::launch_fused(gu, dn, sync, wait_us, static_cast<hipStream_t>(stream)));
 }
 
 int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,

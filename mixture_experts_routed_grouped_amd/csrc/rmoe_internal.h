@@ -34,8 +34,8 @@ hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s);
 hipError_t launch_tile_down(const StageArgs &a, hipStream_t s);
 // Both tiled stages in one persistent launch (gu.y = dn.x = the hidden
 // workspace); sync as described for rmoe_forward_fused_f16; a down tile
-// waits at most wait_ms for its pair's hidden rows.
-hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int wait_ms,
+// waits at most wait_us for its pair's hidden rows.
+hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int64_t wait_us,
                         hipStream_t s);
 
 hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,

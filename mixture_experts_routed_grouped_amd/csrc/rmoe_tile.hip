@@ -527,7 +527,7 @@ hipError_t launch_tile_down(const StageArgs &a, hipStream_t s) {
     return launch<false>(a, (int)((a.N + 255) / 256), s);
 }
 
-hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int wait_ms,
+hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int64_t wait_us,
                         hipStream_t s) {
     unsigned grid = 0;
     hipError_t e = persistent_grid(grid);
@@ -542,7 +542,7 @@ hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
                             (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fused_kernel, dim3(grid), dim3(256), lds, s, gu, dn, sync,
-                       (uint64_t)khz * (uint64_t)wait_ms);
+                       (uint64_t)khz * (uint64_t)wait_us / 1000u);
     return hipGetLastError();
 }
 

@@ -190,7 +190,7 @@ def test_fused_argument_errors_without_gpu():
     odd = ctypes.c_void_p(0x10002)
 
     def fz(H=256, I=128, E=4, Tp=640, pairs=18, M=5, sync=fake, x=fake):
-        return L.rmoe_forward_fused_f16(x, *([fake] * 10), sync, H, I, E, Tp, pairs, M, None)
+        return L.rmoe_forward_fused_f16(x, *([fake] * 10), sync, H, I, E, Tp, pairs, M, 0, None)
 
     assert L.rmoe_fused_sync_words(5) == 16 + 5
     assert L.rmoe_fused_sync_words(-1) == 0

@@ -115,3 +115,39 @@ def test_fused_full_size(name):
     _fused(d, sync)
     assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
     _sync_clean(sync)
+
+
+def test_fused_wait_timeout_from_host():
+    """Failure handling, forced from the host: a 1 µs bound on the down
+    tiles' wait makes them give up while gate/up tiles are still running.
+    The launch still ends, counts the skipped tiles in the error word, writes
+    every hidden row, leaves each skipped output tile untouched (sentinel),
+    and resets the rest of the queue state; the next call on the same buffer
+    with the default bound is complete and exact."""
+    from _gpu_run import SENTINEL
+    cfg = workloads.Config("ftimeout", 3000, 40, 4, 512, 1024, routing="zipf", zipf_s=1.4, seed=5)
+    d = prepare(workloads.make_inputs(cfg))
+    sync = torch.zeros(R.fused_sync_words(d["c"]["num_blocks_m"]), dtype=torch.int32, device="cuda")
+    forward(d, "tile")
+    rows = d["prow"].long()
+    want_out, want_hid = d["out"][rows].clone(), d["hid"][rows].clone()
+    print("[fused] forced wait timeout (1 us)", flush=True)
+    fresh_outputs(d)
+    R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"], d["go"],
+                    d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, max_wait_us=1)
+    torch.cuda.synchronize()
+    s = sync.cpu().numpy()
+    skipped = int(s[R.FUSED_SYNC_ERROR])
+    print(f"[fused] skipped tiles: {skipped}", flush=True)
+    assert skipped > 0, "the forced bound should have expired"
+    s[R.FUSED_SYNC_ERROR] = 0
+    assert not s.any(), "queue state not reset after an aborted launch"
+    assert torch.equal(d["hid"][rows].view(torch.int16), want_hid.view(torch.int16))
+    got = d["out"][rows].view(torch.int16)
+    ok = (got == want_out.view(torch.int16)) | (got == SENTINEL)
+    assert bool(ok.all()), "an aborted launch wrote wrong output values"
+    assert bool((got == SENTINEL).any()), "skipped tiles should leave their rows unwritten"
+    sync.zero_()
+    _fused(d, sync)
+    assert torch.equal(d["out"][rows].view(torch.int16), want_out.view(torch.int16))
+    _sync_clean(sync)
