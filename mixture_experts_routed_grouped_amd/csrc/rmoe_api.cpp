@@ -37,12 +37,17 @@ int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
     return RMOE_OK;
 }
 
-// Kernel family: the weight-streaming family when blocks hold few rows on
-// average (then a weight byte serves at most a handful of tokens and the
-// stage is HBM-bound), the LDS-tiled family otherwise.
+// Kernel family: the weight-streaming family when experts hold few rows on
+// average (then a weight byte serves a handful of tokens and the stage is
+// HBM-bound), the LDS-tiled family otherwise.  Measured crossover (uniform
+// routing; E = 8, 64, 128 with their H, I): streaming is faster up to 24
+// rows per expert and slower from 32, where blocks start to need a second
+// 32-token pass that re-reads the weights.
+constexpr int64_t kStreamMaxRowsPerExpert = 24;
 int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts) {
     if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
-    return pairs <= 48 * (int64_t)num_experts ? RMOE_VARIANT_STREAM : RMOE_VARIANT_TILE;
+    return pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts ? RMOE_VARIANT_STREAM
+                                                                   : RMOE_VARIANT_TILE;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? RMOE_OK : RMOE_ERR_LAUNCH; }

@@ -504,6 +504,24 @@ hipError_t persistent_grid(unsigned &grid) {
     return hipSuccess;
 }
 
+// Rate of the real-time counter (s_memrealtime) on the current device, in
+// kHz (cached per device; 100 MHz where the runtime reports none).
+hipError_t wall_clock_khz(int &khz) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int v = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (v == 0) {
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev);
+        if (e != hipSuccess) return e;
+        if (v <= 0) v = 100000;
+        if (dev < 64) cached[dev].store(v, std::memory_order_relaxed);
+    }
+    khz = v;
+    return hipSuccess;
+}
+
 template <bool DUAL>
 hipError_t launch(const StageArgs &a, int NT, hipStream_t s) {
     unsigned grid = 0;
@@ -532,11 +550,9 @@ hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
     unsigned grid = 0;
     hipError_t e = persistent_grid(grid);
     if (e != hipSuccess) return e;
-    int dev = 0, khz = 0;  // real-time counter rate
-    e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    int khz = 0;
+    e = wall_clock_khz(khz);
     if (e != hipSuccess) return e;
-    if (khz <= 0) khz = 100000;
     const unsigned lds = LDS_BYTES;
     e = hipFuncSetAttribute((const void *)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds);
