@@ -266,6 +266,17 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
     auto stage_row = [&](int row) {
         return smem + (row / RPP) * SLOT + wave * 8192 + (row % RPP) * OB;
     };
+    // down: the routed weights of this lane's tokens, all requested before
+    // any is used, so the epilogue waits for one memory round trip (read
+    // inside the tile loop, the compiler reloaded go[e] and waited for each
+    // dependent load in turn: 8 round trips)
+    [[maybe_unused]] float wtok[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!DUAL) {
+        const float *rwe = a.rw + a.go[b0.e] + toff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (u < ntt && 32 * u + lr < myrows) wtok[u] = rwe[32 * u + lr];
+    }
     // 32x32 accumulator layout: lane holds token column (lane & 31) and,
     // for register 4q + r, weight row 8q + 4lh + r of its 32-row tile t
 #pragma unroll
@@ -287,7 +298,7 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
                 }
             }
         } else {
-            const float w = row < myrows ? a.rw[a.go[b0.e] + toff + row] : 0.f;
+            const float w = wtok[u];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
 #pragma unroll
