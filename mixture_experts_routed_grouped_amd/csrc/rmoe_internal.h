@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace rmoe {
+
+// Opt a kernel into `bytes` of dynamic LDS, once per device: the attribute
+// stays set for the process, so later launches skip the runtime call.
+// `done` is the kernel's own per-device flag word (bit d: device d).
+inline hipError_t lds_opt_in_once(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // One stage of the routed expert FFN as the kernels see it: a grouped GEMM
 // Y[r, n] = epilogue( sum_k X[r, k] * W[e(r), n, k] ) over the valid rows r

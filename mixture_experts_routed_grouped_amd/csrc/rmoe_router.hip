@@ -180,8 +180,8 @@ template <int EP>
 hipError_t launch_ep(const _Float16 *x, const _Float16 *w, int64_t T, int64_t H, int32_t E,
                      int32_t k, int32_t *ids, float *vals, hipStream_t s) {
     using C = RouterCfg<EP>;
-    hipError_t e = hipFuncSetAttribute((const void *)router_kernel<EP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_opt_in_once((const void *)router_kernel<EP>, C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)((T + RT_TOK - 1) / RT_TOK);
     hipLaunchKernelGGL(router_kernel<EP>, dim3(grid), dim3(256), C::LDS_BYTES, s, x, w, T, H, E, k,

@@ -217,8 +217,8 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
 template <bool DUAL, int KS, int D>
 hipError_t launch(const StageArgs &a, hipStream_t s) {
     using C = StreamCfg<DUAL, KS, D>;
-    hipError_t e = hipFuncSetAttribute((const void *)stream_kernel<DUAL, KS, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D>, C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
     hipLaunchKernelGGL((stream_kernel<DUAL, KS, D>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);

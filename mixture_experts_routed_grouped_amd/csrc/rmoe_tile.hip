@@ -539,8 +539,8 @@ hipError_t launch(const StageArgs &a, int NT, hipStream_t s) {
     hipError_t e = persistent_grid(grid);
     if (e != hipSuccess) return e;
     const unsigned lds = LDS_BYTES;  // above the 64 KB default, so opt in
-    e = hipFuncSetAttribute((const void *)tile_kernel<DUAL>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
+    static std::atomic<uint64_t> lds_set{0};
+    e = lds_opt_in_once((const void *)tile_kernel<DUAL>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(tile_kernel<DUAL>, dim3(grid), dim3(256), lds, s, a, NT);
     return hipGetLastError();
@@ -565,8 +565,8 @@ hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
     e = wall_clock_khz(khz);
     if (e != hipSuccess) return e;
     const unsigned lds = LDS_BYTES;
-    e = hipFuncSetAttribute((const void *)fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
+    static std::atomic<uint64_t> lds_set{0};
+    e = lds_opt_in_once((const void *)fused_kernel, (int)lds, lds_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fused_kernel, dim3(grid), dim3(256), lds, s, gu, dn, sync,
                        (uint64_t)khz * (uint64_t)wait_us / 1000u);
