@@ -226,3 +226,36 @@ def test_full_size_sampled(name):
     rel = _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(), o_hid, o_out,
                          name)
     print(f"[full-size] {name}: rel RMS {rel:.2e}", flush=True)
+
+
+def test_pack_large_batch_nontemporal_path():
+    """The large workload packs 1.9 GB of rows, above the size where pack
+    stores them non-temporally: sampled rows equal their token's row bit for
+    bit at the oracle contract's padded position, every routed weight lands
+    at its compact position, and padding rows stay untouched."""
+    import mixture_experts_routed_grouped_amd as R
+    from _gpu_run import SENTINEL
+    cfg = workloads.CONFIGS["large"]
+    inp = workloads.make_inputs(cfg, device="cuda")
+    oc = C.build_contract(inp.topk_ids.tolist(), cfg.experts)
+    prow = np.asarray(oc["padded_row_of_pair"])
+    cpos = np.asarray(oc["compact_pos_of_pair"])
+    Tp, H, k = oc["total_padded_tokens"], cfg.hidden, cfg.top_k
+    assert oc["pairs"] * H * 2 > 512 << 20
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    stacked = torch.full((Tp, H), SENTINEL, dtype=torch.int16, device="cuda").view(torch.float16)
+    wc = torch.zeros(oc["pairs"], dtype=torch.float32, device="cuda")
+    topk_w = torch.from_numpy(np.ascontiguousarray(inp.topk_w.reshape(-1))).cuda()
+    print("[pack] large workload, 131072 pairs", flush=True)
+    R.pack(inp.x, topk_w, i32(prow), i32(cpos), stacked, wc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    sample = np.concatenate([[0, oc["pairs"] - 1], rng.integers(0, oc["pairs"], size=3000)])
+    got = stacked[torch.from_numpy(prow[sample]).long().cuda()].view(torch.int16)
+    want = inp.x[torch.from_numpy(sample // k).long().cuda()].view(torch.int16)
+    assert torch.equal(got, want)
+    wc_host = wc.cpu().numpy()
+    assert np.array_equal(wc_host[cpos], inp.topk_w.reshape(-1).astype(np.float32))
+    valid = torch.zeros(Tp, dtype=torch.bool, device="cuda")
+    valid[torch.from_numpy(prow).long().cuda()] = True
+    assert bool((stacked.view(torch.int16)[~valid] == SENTINEL).all())
