@@ -153,20 +153,21 @@ RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const v
  * prefill-shaped batches.  One persistent kernel runs every gate/up tile,
  * then every down tile; a down tile starts as soon as all gate/up tiles of
  * its own pair of blocks have published their hidden rows, so the two
- * stages overlap at the hand-over and the hidden rows are re-read while they
- * are still in the caches (the workspace is still written: it is the
- * hand-over buffer, not a second output).
+ * stages overlap at the hand-over (the workspace is still written: it is
+ * the hand-over buffer, not a second output).  Results are bit-identical to
+ * the two-launch tiled forward.
  *   sync: int32 device scratch of rmoe_fused_sync_words(num_blocks_m) words,
  *         caller-owned.  It must be all zero before its first use; every
  *         call that runs to completion leaves it zero again, except
  *         sync[RMOE_FUSED_SYNC_ERROR], a sticky count of tiles skipped
  *         because a wait for hidden rows timed out (then every later wait
  *         of that launch gives up at once, so the call still ends).  It is
- *         0 in normal operation; non-zero means out is incomplete.
+ *         0 in normal operation; non-zero means out is incomplete.  Calls
+ *         that share one sync buffer must not overlap in time (use one
+ *         stream, or one buffer each).
  *   max_wait_us: how long a down tile may wait for its pair's hidden rows;
  *         <= 0 selects the default, 2 s (real waits last at most one
- *         gate/up stage, i.e. milliseconds).  Calls that share one sync buffer
- *         must not overlap in time (use one stream, or one buffer each).
+ *         gate/up stage, i.e. milliseconds).
  * Returns as rmoe_forward_f16; the launch is asynchronous, nothing is read
  * back.
  */
