@@ -16,5 +16,9 @@ ref      : ctypes front end of ``moe_ref.c``: the per-row fused expert FFN in
            section 算子来源 (computation semantics) and 完整算子代码 (dtypes).
 brute    : per-(token, expert) dense loop in float64 numpy that uses no
            contract table at all; for tiny inputs.
+combine  : the k-way combine of the expert outputs back into token order
+           (fp32 sum in slot order, one fp16 rounding).
+router   : router logits, softmax over the experts and top-k in float64,
+           from "MetaX-TileLang工具链", section 2.4.
 build    : compiles ``moe_ref.c`` with gcc into ``oracle/_build``.
 """
