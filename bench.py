@@ -259,8 +259,8 @@ def main():
     hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
     out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
     variant = args.variant
-    # the library's automatic choice (pick_variant): streaming up to 24 rows per expert
-    resolved = variant if variant != "auto" else ("stream" if c["pairs"] <= 24 * E else "tile")
+    # the library's automatic choice (pick_variant): streaming up to 32 rows per expert
+    resolved = variant if variant != "auto" else ("stream" if c["pairs"] <= 32 * E else "tile")
 
     def step(evs=None):
         if evs is not None:

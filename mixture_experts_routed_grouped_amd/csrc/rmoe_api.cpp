@@ -17,6 +17,9 @@ constexpr int64_t B = RMOE_BLOCK_M;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 constexpr int32_t kMaxDeviceExperts = 8192;
+#ifndef RMOE_STREAM_MAX_ROWS
+#define RMOE_STREAM_MAX_ROWS 32  // average rows per expert up to which AUTO streams
+#endif
 // default bound on how long a fused down tile waits for its pair's hidden
 // rows (the longest real wait is one gate/up stage: milliseconds)
 constexpr int64_t kFusedWaitUs = 2000000;  // the device contract keeps per-expert tables in LDS
@@ -39,15 +42,21 @@ int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
 
 // Kernel family: the weight-streaming family when experts hold few rows on
 // average (then a weight byte serves a handful of tokens and the stage is
-// HBM-bound), the LDS-tiled family otherwise.  Measured crossover (uniform
-// routing; E = 8, 64, 128 with their H, I): streaming is faster up to 24
-// rows per expert and slower from 32, where blocks start to need a second
-// 32-token pass that re-reads the weights.
-constexpr int64_t kStreamMaxRowsPerExpert = 24;
+// HBM-bound), the LDS-tiled family otherwise.  Streaming passes take 32
+// tokens per pass up to kStreamOneTile rows per expert and 64 beyond, so
+// that blocks of up to 64 rows read their weights once.  Measured crossover
+// (uniform routing): about 48 rows per expert for E=8 (H=4096, I=14336),
+// 40 for E=64 (2048, 1408), 28 for E=128 (7168, 2048); at 32 streaming
+// wins or ties within 2% on all three.
+constexpr int64_t kStreamMaxRowsPerExpert = RMOE_STREAM_MAX_ROWS;
+constexpr int64_t kStreamOneTile = 24;
 int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts) {
     if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
     return pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts ? RMOE_VARIANT_STREAM
                                                                    : RMOE_VARIANT_TILE;
+}
+int stream_tiles(int64_t pairs, int32_t num_experts) {
+    return pairs <= kStreamOneTile * (int64_t)num_experts ? 1 : 2;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? RMOE_OK : RMOE_ERR_LAUNCH; }
@@ -73,7 +82,7 @@ int gate_up_impl(const void *x, const void *gate_w, const void *up_w, const int3
     if (M == 0) return RMOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
-        return to_status(rmoe::launch_stream_gate_up(a, s));
+        return to_status(rmoe::launch_stream_gate_up(a, stream_tiles(pairs, E), s));
     return to_status(rmoe::launch_tile_gate_up(a, s));
 }
 
@@ -99,7 +108,7 @@ int down_impl(const void *workspace, const void *down_w, const float *rw, const 
     if (M == 0) return RMOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
-        return to_status(rmoe::launch_stream_down(a, s));
+        return to_status(rmoe::launch_stream_down(a, stream_tiles(pairs, E), s));
     return to_status(rmoe::launch_tile_down(a, s));
 }
 

@@ -8,16 +8,18 @@
 //     K into contiguous ranges and run independently until the final
 //     reduction (no barrier in the K loop);
 //   * weights travel HBM -> LDS by direct DMA (global_load_lds_dwordx4) in
-//     chunks of K = 64: each instruction reads 8 weight rows x 128 bytes.
-//     Measured on MI355X, that pattern streams from HBM at ~5.9 TB/s, while
-//     loading the MFMA operand layout straight into registers (32 rows x
-//     32 bytes per instruction) reaches ~4 TB/s.  Each wave owns a ring of
+//     chunks of K = 64: each instruction reads 8 weight rows x 128 bytes,
+//     with the non-temporal hint (weights are read once).  Measured on
+//     MI355X, that pattern streams from HBM at ~6.5 TB/s, while loading the
+//     MFMA operand layout straight into registers (32 rows x 32 bytes per
+//     instruction) reaches ~4 TB/s.  Each wave owns a ring of
 //     D chunk slots, refilled D-1 chunks ahead; MFMA operands come back out
 //     of LDS with swizzled, conflict-free ds_read_b128;
-//   * a 32-token tile of the block rides in the same slots (tokens are
-//     shared by all workgroups of the block and come from L2), so every
-//     global read is a DMA and the only waits are the explicit vmcnt ones;
-//     blocks with more than 32 valid rows take one pass per tile;
+//   * the pass's tokens (one 32-token MFMA tile, or two for blocks of up
+//     to 64 rows) ride in the same slots (tokens are shared by all
+//     workgroups of the block and come from L2), so every global read is a
+//     DMA and the only waits are the explicit vmcnt ones; a block with more
+//     rows than a pass holds takes several passes, each reading the weights;
 //   * weights are the MFMA A operand (v_mfma_f32_32x32x16_f16, 32 feature
 //     rows), tokens the B operand; a lane ends up with 4 consecutive
 //     features of one token, so stores are 8-byte fp16 quads;
@@ -51,27 +53,30 @@ constexpr int MF = 32;                // output features per workgroup (MFMA row
 constexpr int CK = 64;                // K per chunk: one 128-byte line per weight row
 constexpr int CHUNK_B = MF * CK * 2;  // 4 KB: one matrix's chunk
 
-template <bool DUAL, int KS, int D>
+// TT: 32-token tiles per pass.  TT = 1 for decode-shaped blocks (~16 rows);
+// TT = 2 for blocks of up to 64 rows, which then read the weights once
+// instead of once per 32-token tile.
+template <bool DUAL, int KS, int D, int TT>
 struct StreamCfg {
-    static constexpr int NM = DUAL ? 2 : 1;            // weight matrices (gate, up)
-    static constexpr int SLOT = (NM + 1) * CHUNK_B;    // weights, then 32 token rows
-    static constexpr int WAVE_LDS = D * SLOT;          // ring of one wave
+    static constexpr int NM = DUAL ? 2 : 1;                 // weight matrices (gate, up)
+    static constexpr int SLOT = (NM + TT) * CHUNK_B;        // weights, then 32*TT token rows
+    static constexpr int WAVE_LDS = D * SLOT;               // ring of one wave
     static constexpr int RING = KS * WAVE_LDS;
-    static constexpr int RED = KS * NM * 16 * 64 * 4;  // partial sums of one tile
+    static constexpr int RED = KS * NM * TT * 16 * 64 * 4;  // partial sums of one pass
     static constexpr int LDS_BYTES = RING > RED ? RING : RED;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-    static_assert((D - 1) * 4 * (NM + 1) < 64, "vmcnt range");
+    static_assert((D - 1) * 4 * (NM + TT) < 64, "vmcnt range");
 };
 
-// One pass: the 32-token tile starting at row p0 of block bx against the 32
+// One pass: the 32*TT tokens starting at row p0 of block bx against the 32
 // features n0.. of the block's expert, over the whole K.  Only the first
-// 8*TD token rows of the tile are moved (TD = ceil(valid rows / 8)): LDS rows
+// 8*TD token rows of the pass are moved (TD = ceil(valid rows / 8)): LDS rows
 // past them keep stale values, which only reach MFMA output columns of
 // tokens that are never stored.
-template <bool DUAL, int KS, int D, int TD>
+template <bool DUAL, int KS, int D, int TT, int TD>
 __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo &bi, int bx, int p0,
                                             int n0, unsigned char *smem, int wave, int lane) {
-    using C = StreamCfg<DUAL, KS, D>;
+    using C = StreamCfg<DUAL, KS, D, TT>;
     constexpr int NM = C::NM;
     constexpr int DMA_PER_CHUNK = 4 * NM + TD;
     const int64_t K = a.K, N = a.N;
@@ -82,49 +87,45 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
     const int c_begin = (nchunks * wave) / KS;
     const int n = (nchunks * (wave + 1)) / KS - c_begin;
 
-    // DMA sources: instruction j of matrix m (m = NM: the token tile) moves
-    // rows 8j .. 8j+7 of the chunk; lane i takes row 8j + i/8 and physical
-    // chunk i%8, i.e. logical chunk (i%8) ^ swz(row).  Token rows past the
-    // valid ones are read (they lie inside the block) but never stored.
-    const _Float16 *src[NM + 1][4];
+    // DMA sources: instruction j of a weight matrix m moves rows 8j .. 8j+7
+    // of its chunk, instruction j of the tokens rows 8j .. 8j+7 of the pass;
+    // lane i takes row 8j + i/8 and physical chunk i%8, i.e. logical chunk
+    // (i%8) ^ swz(row).  Token rows past the valid ones are read (they lie
+    // inside the block) but never stored.
+    const _Float16 *wsrc[NM][4], *tsrc[4 * TT];
 #pragma unroll
-    for (int m = 0; m <= NM; ++m)
+    for (int j = 0; j < 4 * TT; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ lds_swz(r);
+        if (j < 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 8 * j + (lane >> 3);
-            const int c = (lane & 7) ^ lds_swz(r);
-            int64_t row;
-            const _Float16 *mat;
-            if (m == NM) {
-                mat = a.x;
-                row = (int64_t)bx * kBlockM + p0 + r;
-            } else {
-                mat = m ? a.w1 : a.w0;
-                row = (int64_t)bi.e * N + n0 + r;
-            }
-            src[m][j] = mat + row * K + (int64_t)c_begin * CK + 8 * c;
+            for (int m = 0; m < NM; ++m)
+                wsrc[m][j] = (m ? a.w1 : a.w0) + ((int64_t)bi.e * N + n0 + r) * K +
+                             (int64_t)c_begin * CK + 8 * c;
         }
+        tsrc[j] = a.x + ((int64_t)bx * kBlockM + p0 + r) * K + (int64_t)c_begin * CK + 8 * c;
+    }
     const unsigned wbase = (unsigned)(uintptr_t)smem + wave * C::WAVE_LDS;
     const unsigned char *wring = smem + wave * C::WAVE_LDS;
     auto dma_chunk = [&](int i, int slot) {
+        const unsigned sb = wbase + slot * C::SLOT;
+        // weight rows are read once: non-temporal; token rows are shared by
+        // every slice of the block: cached normally
 #pragma unroll
-        for (int m = 0; m <= NM; ++m)
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int j = 0; j < (m == NM ? TD : 4); ++j) {
-                // weight rows are read once: non-temporal; token rows are
-                // shared by every slice of the block: cached normally
-                if (m == NM)
-                    dma16(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
-                else
-                    dma16_nt(src[m][j] + (int64_t)i * CK, wbase + slot * C::SLOT + m * CHUNK_B + 8 * j * 128);
-            }
+            for (int j = 0; j < 4; ++j) dma16_nt(wsrc[m][j] + (int64_t)i * CK, sb + m * CHUNK_B + 8 * j * 128);
+#pragma unroll
+        for (int j = 0; j < TD; ++j) dma16(tsrc[j] + (int64_t)i * CK, sb + NM * CHUNK_B + 8 * j * 128);
     };
 
-    f16x acc[NM];
+    f16x acc[NM][TT];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
 
     if (n > 0) {
 #pragma unroll
@@ -136,64 +137,74 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
             dma_chunk(min(i + D - 1, n - 1), (i + D - 1) % D);
             wait_vm<(D - 1) * DMA_PER_CHUNK>();
             const unsigned char *slot = wring + (i % D) * C::SLOT;
-            h8 af[NM][4], bf[4];
+            h8 af[NM][4], bf[TT][4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int off = lds_off(lr, 2 * s + lh);
 #pragma unroll
                 for (int m = 0; m < NM; ++m) af[m][s] = *(const h8 *)(slot + m * CHUNK_B + off);
-                bf[s] = *(const h8 *)(slot + NM * CHUNK_B + off);
+#pragma unroll
+                for (int t = 0; t < TT; ++t)
+                    bf[t][s] = *(const h8 *)(slot + NM * CHUNK_B + lds_off(32 * t + lr, 2 * s + lh));
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
-                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m][s], bf[s], acc[m], 0, 0, 0);
+                for (int t = 0; t < TT; ++t)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+                        acc[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[m][s], bf[t][s], acc[m][t], 0, 0, 0);
         }
     }
     wait_vm<0>();  // no DMA may land in the ring once it holds partial sums
     __syncthreads();
 
     // ---- fixed-order reduction of the KS partial sums; output quad q (4
-    //      features) belongs to wave q % KS
-    float *red = reinterpret_cast<float *>(smem);  // [KS][NM][16][64]
+    //      features) of token tile t belongs to wave (4 t + q) % KS
+    float *red = reinterpret_cast<float *>(smem);  // [KS][NM][TT][16][64]
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((wave * NM + m) * 16 + r) * 64 + lane] = acc[m][r];
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(((wave * NM + m) * TT + t) * 16 + r) * 64 + lane] = acc[m][t][r];
     __syncthreads();
-    const int tok = p0 + lr;
+    [[maybe_unused]] const float *rwe = DUAL ? nullptr : a.rw + a.go[bi.e] + bi.token_offset;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (q % KS != wave || tok >= bi.rows) continue;
-        float v[NM][4];
+    for (int t = 0; t < TT; ++t) {
+        const int tok = p0 + 32 * t + lr;
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int q = 0; q < 4; ++q) {
+            if ((4 * t + q) % KS != wave || tok >= bi.rows) continue;
+            float v[NM][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float s = red[((0 * NM + m) * 16 + 4 * q + r) * 64 + lane];
+            for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int w = 1; w < KS; ++w) s += red[((w * NM + m) * 16 + 4 * q + r) * 64 + lane];
-                v[m][r] = s;
+                for (int r = 0; r < 4; ++r) {
+                    float s = red[(((0 * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < KS; ++w) s += red[(((w * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
+                    v[m][r] = s;
+                }
+            // 32x32 accumulator layout: register 4q + r holds feature 8q + 4lh + r
+            const int64_t row = (int64_t)bx * kBlockM + tok;
+            _Float16 *dst = a.y + row * N + n0 + 8 * q + 4 * lh;
+            h4 o;
+            if constexpr (DUAL) {
+                o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1], silu(v[0][2]) * v[1][2],
+                          silu(v[0][3]) * v[1][3]);
+            } else {
+                const float w = rwe[tok];
+                o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
             }
-        // 32x32 accumulator layout: register 4q + r holds feature 8q + 4lh + r
-        const int64_t row = (int64_t)bx * kBlockM + tok;
-        _Float16 *dst = a.y + row * N + n0 + 8 * q + 4 * lh;
-        h4 o;
-        if constexpr (DUAL) {
-            o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1], silu(v[0][2]) * v[1][2],
-                      silu(v[0][3]) * v[1][3]);
-        } else {
-            const float w = a.rw[a.go[bi.e] + bi.token_offset + tok];
-            o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
+            *reinterpret_cast<h4 *>(dst) = o;
         }
-        *reinterpret_cast<h4 *>(dst) = o;
     }
     __syncthreads();  // the next pass refills the ring that holds red[]
 }
 
 // grid: (N / 32, num_blocks_m); block: 64 * KS threads; dynamic LDS LDS_BYTES.
-template <bool DUAL, int KS, int D>
+template <bool DUAL, int KS, int D, int TT>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int bx = blockIdx.y;
@@ -204,35 +215,48 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int n0 = blockIdx.x * MF;
-    for (int p0 = 0; p0 < bi.rows; p0 += 32) {
-        switch ((min(bi.rows - p0, 32) + 7) / 8) {  // token DMA rows of this pass, in 8s
-            case 1: stream_pass<DUAL, KS, D, 1>(a, bi, bx, p0, n0, smem, wave, lane); break;
-            case 2: stream_pass<DUAL, KS, D, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
-            case 3: stream_pass<DUAL, KS, D, 3>(a, bi, bx, p0, n0, smem, wave, lane); break;
-            default: stream_pass<DUAL, KS, D, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
+    for (int p0 = 0; p0 < bi.rows; p0 += 32 * TT) {
+        // token DMA rows of this pass, in 8s
+        const int td = (min(bi.rows - p0, 32 * TT) + 7) / 8;
+        if constexpr (TT == 1) {
+            switch (td) {
+                case 1: stream_pass<DUAL, KS, D, 1, 1>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                case 2: stream_pass<DUAL, KS, D, 1, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                case 3: stream_pass<DUAL, KS, D, 1, 3>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                default: stream_pass<DUAL, KS, D, 1, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            }
+        } else {
+            switch ((td + 1) / 2) {  // in 16s: fewer instances, at most 8 extra rows moved
+                case 1: stream_pass<DUAL, KS, D, 2, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                case 2: stream_pass<DUAL, KS, D, 2, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                case 3: stream_pass<DUAL, KS, D, 2, 6>(a, bi, bx, p0, n0, smem, wave, lane); break;
+                default: stream_pass<DUAL, KS, D, 2, 8>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            }
         }
     }
 }
 
-template <bool DUAL, int KS, int D>
+template <bool DUAL, int KS, int D, int TT>
 hipError_t launch(const StageArgs &a, hipStream_t s) {
-    using C = StreamCfg<DUAL, KS, D>;
+    using C = StreamCfg<DUAL, KS, D, TT>;
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D>, C::LDS_BYTES, lds_set);
+    hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D, TT>, C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
-    hipLaunchKernelGGL((stream_kernel<DUAL, KS, D>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL((stream_kernel<DUAL, KS, D, TT>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_stream_gate_up(const StageArgs &a, hipStream_t s) {
-    return launch<true, RMOE_GU_KS, RMOE_GU_D>(a, s);
+hipError_t launch_stream_gate_up(const StageArgs &a, int tiles, hipStream_t s) {
+    return tiles == 2 ? launch<true, RMOE_GU_KS, RMOE_GU_D, 2>(a, s)
+                      : launch<true, RMOE_GU_KS, RMOE_GU_D, 1>(a, s);
 }
 
-hipError_t launch_stream_down(const StageArgs &a, hipStream_t s) {
-    return launch<false, RMOE_DN_KS, RMOE_DN_D>(a, s);
+hipError_t launch_stream_down(const StageArgs &a, int tiles, hipStream_t s) {
+    return tiles == 2 ? launch<false, RMOE_DN_KS, RMOE_DN_D, 2>(a, s)
+                      : launch<false, RMOE_DN_KS, RMOE_DN_D, 1>(a, s);
 }
 
 }  // namespace rmoe

@@ -112,6 +112,14 @@ def test_single_expert_and_no_pairs(variant):
     _full_compare(workloads.make_inputs(cfg, topk_ids=ids), variant)
 
 
+@pytest.mark.parametrize("T,E,k", [(128, 8, 2), (96, 6, 2)])
+def test_auto_mid_batch(T, E, k):
+    """25-32 routed rows per expert on average: the automatic choice streams
+    with 64-token passes (two MFMA token tiles per pass)."""
+    cfg = workloads.Config(f"mid{T}", T, E, k, 512, 1024, routing="uniform", seed=12)
+    _full_compare(workloads.make_inputs(cfg), "auto")
+
+
 def test_determinism():
     cfg = workloads.Config("det", 400, 6, 2, 256, 256, routing="zipf", zipf_s=1.3, seed=8)
     inp = workloads.make_inputs(cfg)
