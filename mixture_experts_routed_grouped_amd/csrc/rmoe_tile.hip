@@ -38,10 +38,7 @@
 #include "../../include/routed_moe.h"
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
-
-#ifndef RMOE_TILE_GROUP
-#define RMOE_TILE_GROUP 8   // weight slices per locality group (see tile_kernel)
-#endif
+#include "rmoe_sched.h"
 
 namespace rmoe {
 namespace {
@@ -65,6 +62,7 @@ constexpr int SUB = BK / 16;                // MFMA sub-steps per K step
 constexpr int VM_ALLOW = DMA_HALF;
 constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc1 (device scope)
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+static_assert(kItemRows == kBlockM, "work items are contract blocks");
 
 // One tile: blocks bx (b0: its expert, offset in the group, valid rows) and
 // bx+1 (rows1 valid rows; has1: it belongs to the same expert) against the
@@ -333,62 +331,30 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
     }
 }
 
-// Live pairs of expert e: its blocks with valid rows, two per pair.
-__device__ __forceinline__ int pairs_of(const StageArgs &a, int e) {
-    return ((a.gs[e] + kBlockM - 1) / kBlockM + 1) / 2;
-}
-
-// Work item -> (weight slice, pair).  Items are listed slice group by slice
-// group (RMOE_TILE_GROUP slices), pairs in expert order within a group, the
-// group's slices innermost.  (ce, cp0) is a cursor -- an expert and the index
-// of its first pair -- that only moves forward while the items do.
-struct ItemPos {
-    int nt, bx, rows1;
+// Runs work item it (rmoe_sched.h) with the workgroup's LDS.
+template <bool DUAL, bool WT = false>
+__device__ __forceinline__ void run_item(const StageArgs &a, unsigned char *smem, const TileItem &it) {
     BlockInfo b0;
-};
-__device__ __forceinline__ ItemPos decode_item(const StageArgs &a, int P, int NT, int item, int &ce,
-                                               int &cp0) {
-    const int gsz = RMOE_TILE_GROUP * P;
-    const int g = item / gsz, r = item - g * gsz;
-    const int width = min(RMOE_TILE_GROUP, NT - g * RMOE_TILE_GROUP);
-    const int p = r / width;
-    ItemPos it;
-    it.nt = g * RMOE_TILE_GROUP + (r - p * width);
-    if (p < cp0) ce = cp0 = 0;  // a new slice group starts the pairs again
-    while (p >= cp0 + pairs_of(a, ce)) {
-        cp0 += pairs_of(a, ce);
-        ++ce;
-    }
-    const int q = p - cp0, gse = a.gs[ce];
-    it.b0.e = ce;
-    it.b0.token_offset = 2 * kBlockM * q;
-    it.b0.rows = min(kBlockM, gse - it.b0.token_offset);
-    it.rows1 = max(0, min(kBlockM, gse - it.b0.token_offset - kBlockM));
-    it.bx = a.gpo[ce] / kBlockM + 2 * q;
-    return it;
+    b0.e = it.e;
+    b0.token_offset = it.off;
+    b0.rows = it.rows0;
+    run_tile<DUAL, WT>(a, smem, it.nt, it.bx, b0, it.rows1 > 0, it.rows1);
 }
 
 // Persistent kernel: one workgroup per CU (a multiple of 8 of them, LDS_BYTES
 // of dynamic LDS each), looping over work items, all live: a pair of blocks
 // of one expert that holds valid rows, times a weight slice (NT = N / 128
-// slices for gate/up, ceil(N / 256) for down).  The item list is cut into 8
-// contiguous parts, one per XCD (workgroup w runs on XCD w % 8), so the 32
-// workgroups of an XCD run a rectangle of 4 consecutive pairs x 8 slices at
-// a time -- operands they share in that XCD's L2.
+// slices for gate/up, ceil(N / 256) for down).  The item list (rmoe_sched.h)
+// is cut into 8 contiguous parts, one per XCD (workgroup w runs on XCD
+// w % 8), so the 32 workgroups of an XCD run a rectangle of 4 consecutive
+// pairs x 8 slices at a time -- operands they share in that XCD's L2.
 template <bool DUAL>
 __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    int P = 0;
-    for (int e = 0; e < a.E; ++e) P += pairs_of(a, e);
-    const int total = P * NT;
-    const int per = (total + kXcd - 1) / kXcd;
-    const int xcd = blockIdx.x % kXcd, lane_of_xcd = blockIdx.x / kXcd, nl = gridDim.x / kXcd;
-    const int end = min(total, (xcd + 1) * per);
-    int ce = 0, cp0 = 0;
-    for (int item = xcd * per + lane_of_xcd; item < end; item += nl) {
-        const ItemPos it = decode_item(a, P, NT, item, ce, cp0);
-        run_tile<DUAL>(a, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
-    }
+    const TileSeq seq = tile_seq(a.gs, a.E, NT, blockIdx.x % kXcd, kXcd);
+    const int nl = gridDim.x / kXcd;
+    TileCursor cur;
+    for (int i = blockIdx.x / kXcd; i < seq.n; i += nl) run_item<DUAL>(a, smem, tile_item(a.gs, a.gpo, seq, i, cur));
 }
 
 // ---- Both stages in one launch.
@@ -421,14 +387,10 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
     int32_t *tickets = sync + RMOE_FUSED_SYNC_TICKETS;
     int32_t *done = sync + RMOE_FUSED_SYNC_HEAD;
     const int NT1 = (int)(gu.N / 128), NT2 = (int)((dn.N + 255) / 256);
-    int P = 0;
-    for (int e = 0; e < gu.E; ++e) P += pairs_of(gu, e);
     const int grp = blockIdx.x % kXcd;
-    const int total1 = P * NT1, total2 = P * NT2;
-    const int per1 = (total1 + kXcd - 1) / kXcd, per2 = (total2 + kXcd - 1) / kXcd;
-    const int lo1 = grp * per1, lo2 = grp * per2;
-    const int n1 = max(0, min(total1, lo1 + per1) - lo1), n2 = max(0, min(total2, lo2 + per2) - lo2);
-    int ce = 0, cp0 = 0;
+    const TileSeq seq1 = tile_seq(gu.gs, gu.E, NT1, grp, kXcd), seq2 = tile_seq(dn.gs, dn.E, NT2, grp, kXcd);
+    const int n1 = seq1.n, n2 = seq2.n;
+    TileCursor cur;
     for (;;) {
         __syncthreads();  // every wave is done with the LDS of the last item
         if (threadIdx.x == 0)
@@ -438,9 +400,9 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
         const int t = bcast[0];
         if (t >= n1 + n2) break;
         if (t < n1) {
-            const ItemPos it = decode_item(gu, P, NT1, lo1 + t, ce, cp0);
+            const TileItem it = tile_item(gu.gs, gu.gpo, seq1, t, cur);
             __syncthreads();  // the ticket is read before the DMAs reuse its LDS word
-            run_tile<true, true>(gu, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
+            run_item<true, true>(gu, smem, it);
             // the hidden rows went out write-through at device scope; once
             // every wave's stores have completed they are visible to all
             // XCDs, and the count may go up (no L2 write-back needed)
@@ -449,7 +411,7 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
             if (threadIdx.x == 0)
                 __hip_atomic_fetch_add(done + it.bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            const ItemPos it = decode_item(dn, P, NT2, lo2 + (t - n1), ce, cp0);
+            const TileItem it = tile_item(dn.gs, dn.gpo, seq2, t - n1, cur);
             if (threadIdx.x == 0) {
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                 bool ready;
@@ -477,7 +439,7 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
             const bool ready = bcast[1] != 0;
             __syncthreads();  // the flag is read before the DMAs reuse its LDS word
             if (!ready) continue;
-            run_tile<false>(dn, smem, it.nt, it.bx, it.b0, it.rows1 > 0, it.rows1);
+            run_item<false>(dn, smem, it);
         }
     }
     // the last workgroup out resets the queue state (the error word stays)
