@@ -32,7 +32,7 @@ METRIC = "fused MoE TFLOP/s (useful 6·pairs·H·I) + % MFMA/HBM roofline, 1×MI
 # sources that define a variant's kernels: a traffic record is valid only for
 # the exact sources it was measured on
 KERNEL_SOURCES = {"stream": ["rmoe_stream.hip", "rmoe_device.h"],
-                  "tile": ["rmoe_tile.hip", "rmoe_device.h"]}
+                  "tile": ["rmoe_tile.hip", "rmoe_device.h", "rmoe_sched.h"]}
 
 
 def parse():
