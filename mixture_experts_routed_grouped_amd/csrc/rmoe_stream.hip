@@ -4,9 +4,12 @@
 // read the routed experts' weights from HBM once, so this family is built
 // around the access pattern HBM serves fastest.
 //
-//   * one workgroup = one 128-row block x 32 output features; KS waves split
-//     K into contiguous ranges and run independently until the final
-//     reduction (no barrier in the K loop);
+//   * one workgroup = one 128-row block x FT tiles of 32 output features
+//     (gate/up: one tile, its gate and up rows; down: two tiles, so each
+//     token chunk serves twice the weight bytes -- down 155 -> 147 us on a
+//     decode batch, while a second gate/up tile measured 1.5% slower); KS
+//     waves split K into contiguous ranges and run independently until the
+//     final reduction (no barrier in the K loop);
 //   * weights travel HBM -> LDS by direct DMA (global_load_lds_dwordx4) in
 //     chunks of K = 64: each instruction reads 8 weight rows x 128 bytes,
 //     with the non-temporal hint (weights are read once).  Measured on
@@ -45,6 +48,17 @@
 #ifndef RMOE_DN_D
 #define RMOE_DN_D 2
 #endif
+// 32-feature weight tiles per workgroup, by stage and pass width (the
+// 64-token pass of gate/up has no LDS room for a second tile)
+#ifndef RMOE_GU_FT1
+#define RMOE_GU_FT1 1
+#endif
+#ifndef RMOE_DN_FT1
+#define RMOE_DN_FT1 2
+#endif
+#ifndef RMOE_DN_FT2
+#define RMOE_DN_FT2 2
+#endif
 
 namespace rmoe {
 namespace {
@@ -58,7 +72,9 @@ constexpr int CHUNK_B = MF * CK * 2;  // 4 KB: one matrix's chunk
 // instead of once per 32-token tile.
 template <bool DUAL, int KS, int D, int TT>
 struct StreamCfg {
-    static constexpr int NM = DUAL ? 2 : 1;                 // weight matrices (gate, up)
+    static constexpr int FT = DUAL ? (TT == 1 ? RMOE_GU_FT1 : 1) : (TT == 1 ? RMOE_DN_FT1 : RMOE_DN_FT2);
+    static constexpr int G = DUAL ? 2 : 1;                  // matrices per feature tile: gate and up, or down
+    static constexpr int NM = G * FT;                       // weight tiles: matrix g of feature tile f is g + G f
     static constexpr int SLOT = (NM + TT) * CHUNK_B;        // weights, then 32*TT token rows
     static constexpr int WAVE_LDS = D * SLOT;               // ring of one wave
     static constexpr int RING = KS * WAVE_LDS;
@@ -100,7 +116,7 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
         if (j < 4) {
 #pragma unroll
             for (int m = 0; m < NM; ++m)
-                wsrc[m][j] = (m ? a.w1 : a.w0) + ((int64_t)bi.e * N + n0 + r) * K +
+                wsrc[m][j] = (m % C::G ? a.w1 : a.w0) + ((int64_t)bi.e * N + n0 + 32 * (m / C::G) + r) * K +
                              (int64_t)c_begin * CK + 8 * c;
         }
         tsrc[j] = a.x + ((int64_t)bx * kBlockM + p0 + r) * K + (int64_t)c_begin * CK + 8 * c;
@@ -174,36 +190,42 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
     for (int t = 0; t < TT; ++t) {
         const int tok = p0 + 32 * t + lr;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if ((4 * t + q) % KS != wave || tok >= bi.rows) continue;
-            float v[NM][4];
+        for (int f = 0; f < C::FT; ++f) {
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+            for (int q = 0; q < 4; ++q) {
+                if ((4 * (t * C::FT + f) + q) % KS != wave || tok >= bi.rows) continue;
+                // the matrices this output needs: gate and up, or down, of tile f
+                float v[C::G][4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float s = red[(((0 * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
+                for (int mm = 0; mm < C::G; ++mm) {
+                    const int m = mm + C::G * f;
 #pragma unroll
-                    for (int w = 1; w < KS; ++w) s += red[(((w * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
-                    v[m][r] = s;
+                    for (int r = 0; r < 4; ++r) {
+                        float s = red[(((0 * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
+#pragma unroll
+                        for (int w = 1; w < KS; ++w) s += red[(((w * NM + m) * TT + t) * 16 + 4 * q + r) * 64 + lane];
+                        v[mm][r] = s;
+                    }
                 }
-            // 32x32 accumulator layout: register 4q + r holds feature 8q + 4lh + r
-            const int64_t row = (int64_t)bx * kBlockM + tok;
-            _Float16 *dst = a.y + row * N + n0 + 8 * q + 4 * lh;
-            h4 o;
-            if constexpr (DUAL) {
-                o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1], silu(v[0][2]) * v[1][2],
-                          silu(v[0][3]) * v[1][3]);
-            } else {
-                const float w = rwe[tok];
-                o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
+                // 32x32 accumulator layout: register 4q + r holds feature 8q + 4lh + r
+                const int64_t row = (int64_t)bx * kBlockM + tok;
+                _Float16 *dst = a.y + row * N + n0 + 32 * f + 8 * q + 4 * lh;
+                h4 o;
+                if constexpr (DUAL) {
+                    o = to_h4(silu(v[0][0]) * v[1][0], silu(v[0][1]) * v[1][1], silu(v[0][2]) * v[1][2],
+                              silu(v[0][3]) * v[1][3]);
+                } else {
+                    const float w = rwe[tok];
+                    o = to_h4(v[0][0] * w, v[0][1] * w, v[0][2] * w, v[0][3] * w);
+                }
+                *reinterpret_cast<h4 *>(dst) = o;
             }
-            *reinterpret_cast<h4 *>(dst) = o;
         }
     }
     __syncthreads();  // the next pass refills the ring that holds red[]
 }
 
-// grid: (N / 32, num_blocks_m); block: 64 * KS threads; dynamic LDS LDS_BYTES.
+// grid: (N / (32 FT), num_blocks_m); block: 64 * KS threads; dynamic LDS LDS_BYTES.
 template <bool DUAL, int KS, int D, int TT>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     // loop bounds in scalar registers (uniform branches)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * MF;
+    const int n0 = blockIdx.x * MF * StreamCfg<DUAL, KS, D, TT>::FT;
     for (int p0 = 0; p0 < bi.rows; p0 += 32 * TT) {
         // token DMA rows of this pass, in 8s
         const int td = (min(bi.rows - p0, 32 * TT) + 7) / 8;
@@ -242,7 +264,7 @@ hipError_t launch(const StageArgs &a, hipStream_t s) {
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D, TT>, C::LDS_BYTES, lds_set);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(a.N / MF), (unsigned)a.M);
+    dim3 grid((unsigned)(a.N / (MF * C::FT)), (unsigned)a.M);
     hipLaunchKernelGGL((stream_kernel<DUAL, KS, D, TT>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
