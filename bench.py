@@ -232,8 +232,8 @@ def main():
         calibrate_copy(args.calibrate_copy_mib, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this routed-kernel build has no multi-GPU path "
-              "(expert/tensor sharding is a design note, not code). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert or tensor sharding is described, not implemented). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -13,7 +13,7 @@ section 完整算子代码, plus the section 实现要点 (padded vs compact ind
 Plain Python lists and loops on purpose: this is the definition, not a fast
 implementation.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * group_offsets / group_padded_offsets carry E+1 entries, the last being the
     total (the kernel signature declares num_experts+1 entries; the tutorial
     script builds only E).  The kernel reads entries [0, E) only.

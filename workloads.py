@@ -6,7 +6,7 @@ per token), routed weights, token rows and expert weights.  Building the
 dispatch contract, packing and the FFN itself are done separately by the
 oracle and by the HIP library.
 
-Recipe (stated with the workload list in the design doc):
+Recipe:
   * routing: every token picks k distinct experts.  The tiny case uses
     CPython ``random.Random(seed).sample(range(E), k)`` per token, as the
     tutorial's contract script does.  The others draw per-token successive
