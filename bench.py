@@ -120,9 +120,11 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
     r_ids = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.int32, device=dev)
     r_w = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev)
 
+    c_buf = R.build_contract_device(r_ids, cfg.experts)  # reused: the layer allocates nothing
+
     def layer():
         R.router(inp.x, wr, cfg.top_k, r_ids, r_w)
-        c = R.build_contract_device(r_ids, cfg.experts)
+        c = R.build_contract_device(r_ids, cfg.experts, out=c_buf)
         R.pack(inp.x, r_w.reshape(-1), c["padded_row_of_pair"], c["compact_pos_of_pair"], stacked,
                w_compact)
         R.gate_up(stacked, inp.wg, inp.wu, c["group_sizes"], c["group_padded_offsets"],
@@ -133,7 +135,7 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
 
     steps = {
         "router": lambda: R.router(inp.x, wr, cfg.top_k, r_ids, r_w),
-        "contract_device": lambda: R.build_contract_device(ids, cfg.experts),
+        "contract_device": lambda: R.build_contract_device(ids, cfg.experts, out=c_buf),
         "pack": lambda: R.pack(inp.x, topk_w, d["padded_row_of_pair"], d["compact_pos_of_pair"],
                                stacked, w_compact),
         "combine": lambda: R.combine(out, d["padded_row_of_pair"], cfg.top_k, y),

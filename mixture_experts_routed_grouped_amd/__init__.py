@@ -343,14 +343,17 @@ def contract_workspace_bytes(num_pairs: int, num_experts: int) -> int:
     return int(lib().rmoe_contract_workspace_bytes(num_pairs, num_experts))
 
 
-def build_contract_device(topk_ids, num_experts: int, stream=None) -> dict:
+def build_contract_device(topk_ids, num_experts: int, stream=None, out=None) -> dict:
     """The dispatch contract built on the GPU from device top-k ids
     ``[T, k]`` int32.  Returns device int32 tensors ``group_sizes``,
     ``group_offsets``, ``group_padded_offsets``, ``group_idx_for_bx``,
     ``order``, ``padded_row_of_pair``, ``compact_pos_of_pair``, ``bad_ids``
     (one entry: pairs with an expert id outside [0, E), which the tables
     leave out) and the host ints ``num_blocks_m``, ``total_padded_tokens``
-    and ``pairs``.  Asynchronous on ``stream``; no host round trip."""
+    and ``pairs``.  Asynchronous on ``stream``; no host round trip.
+    ``out``: a dict an earlier call returned for the same T, k and E; its
+    tensors (scratch included) are filled again and returned, so the call
+    allocates nothing.  The earlier tables are overwritten in stream order."""
     torch = _torch()
     if topk_ids.dim() != 2:
         raise ValueError("topk_ids must be [T, k]")
@@ -358,14 +361,20 @@ def build_contract_device(topk_ids, num_experts: int, stream=None) -> dict:
     pairs, E = T * k, int(num_experts)
     M = -(-pairs // BLOCK_M) + E
     dev = topk_ids.device
-    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=dev)[:n]
-    out = {"group_sizes": i32(E), "group_offsets": i32(E + 1), "group_padded_offsets": i32(E + 1),
-           "group_idx_for_bx": i32(M), "order": i32(pairs), "padded_row_of_pair": i32(pairs),
-           "compact_pos_of_pair": i32(pairs), "bad_ids": i32(1)}
     nbytes = contract_workspace_bytes(pairs, E)
     if nbytes == 0:
         raise RmoeError(f"device contract: unsupported expert count {E}")
-    ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=dev)
+    if out is not None:
+        if (out.get("pairs"), out.get("num_blocks_m"), out["group_sizes"].numel()) != (pairs, M, E) \
+                or out["_workspace"].device != dev:
+            raise ValueError("out was built for another shape or device")
+        ws = out["_workspace"]
+    else:
+        i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=dev)[:n]
+        out = {"group_sizes": i32(E), "group_offsets": i32(E + 1), "group_padded_offsets": i32(E + 1),
+               "group_idx_for_bx": i32(M), "order": i32(pairs), "padded_row_of_pair": i32(pairs),
+               "compact_pos_of_pair": i32(pairs), "bad_ids": i32(1)}
+        ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=dev)
     nb = ctypes.c_int32(0)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
     st = lib().rmoe_build_contract_device(

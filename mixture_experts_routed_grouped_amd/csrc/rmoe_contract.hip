@@ -17,6 +17,8 @@
 //      <= bx*128 (binary search over the strictly increasing starts).
 // Pairs whose expert id lies outside [0, E) are left out of every table,
 // get -1 as padded row and compact position, and are counted in *bad.
+// A batch that fits one chunk (decode-sized) runs all four steps in one
+// workgroup and one launch, with the same arithmetic.
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
@@ -25,6 +27,7 @@ namespace {
 
 constexpr int TPB = 256;
 constexpr int CHUNK = 2048;  // pairs per chunk
+constexpr int SMALL_E = 1024;  // expert bound of the one-launch path (its LDS)
 
 __global__ __launch_bounds__(TPB) void hist_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                    int32_t E, int32_t *__restrict__ cc,
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(TPB) void scatter_kernel(const int32_t *__restrict_
     for (int e = threadIdx.x; e < E; e += TPB) base[e] = go[e] + cc[(int64_t)blockIdx.x * E + e];
     __syncthreads();
     const int64_t c0 = (int64_t)blockIdx.x * CHUNK;
-    for (int sub = 0; sub < CHUNK; sub += TPB) {
+    for (int sub = 0; sub < CHUNK && c0 + sub < pairs; sub += TPB) {  // uniform bound
         const int64_t p = c0 + sub + threadIdx.x;
         const int32_t e = p < pairs ? ids[p] : -1;
         const bool valid = e >= 0 && e < E;
@@ -159,6 +162,112 @@ __global__ __launch_bounds__(TPB) void blocks_kernel(const int32_t *__restrict__
     gidx[bx] = lo;
 }
 
+// All four steps for a batch of at most CHUNK pairs and at most SMALL_E
+// experts: one workgroup, tables kept in LDS between the steps.
+__global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__restrict__ ids,
+                                                             int32_t pairs, int32_t E, int32_t M,
+                                                             int32_t *__restrict__ gs,
+                                                             int32_t *__restrict__ go,
+                                                             int32_t *__restrict__ gpo,
+                                                             int32_t *__restrict__ gidx,
+                                                             int32_t *__restrict__ order,
+                                                             int32_t *__restrict__ prow,
+                                                             int32_t *__restrict__ cpos,
+                                                             int32_t *__restrict__ bad) {
+    __shared__ int32_t h[SMALL_E + 1];    // counts (+ out-of-range), then next position
+    __shared__ int32_t lgo[SMALL_E + 1], lgpo[SMALL_E + 1];
+    __shared__ int32_t part_c[TPB], part_p[TPB], eid[TPB];
+    // 1. histogram
+    for (int e = threadIdx.x; e <= E; e += TPB) h[e] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < pairs; p += TPB) {
+        const int32_t e = ids[p];
+        atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
+    }
+    __syncthreads();
+    // 2. totals and the two exclusive scans over the experts
+    const int seg = (E + TPB - 1) / TPB;
+    const int e0 = min(E, (int)threadIdx.x * seg), e1 = min(E, e0 + seg);
+    int32_t sc = 0, sp = 0;
+    for (int e = e0; e < e1; ++e) {
+        gs[e] = h[e];
+        sc += h[e];
+        sp += (h[e] / kBlockM + 1) * kBlockM;  // ceil((c+1)/128)*128
+    }
+    part_c[threadIdx.x] = sc;
+    part_p[threadIdx.x] = sp;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t rc = 0, rp = 0;
+        for (int i = 0; i < TPB; ++i) {
+            const int32_t vc = part_c[i], vp = part_p[i];
+            part_c[i] = rc;
+            part_p[i] = rp;
+            rc += vc;
+            rp += vp;
+        }
+        go[E] = lgo[E] = rc;
+        gpo[E] = lgpo[E] = rp;
+        *bad = h[E];
+    }
+    __syncthreads();
+    {
+        int32_t rc = part_c[threadIdx.x], rp = part_p[threadIdx.x];
+        for (int e = e0; e < e1; ++e) {
+            go[e] = lgo[e] = rc;
+            gpo[e] = lgpo[e] = rp;
+            rc += h[e];
+            rp += (h[e] / kBlockM + 1) * kBlockM;
+        }
+    }
+    __syncthreads();  // every count was read: h[] becomes the next compact position
+    for (int e = threadIdx.x; e < E; e += TPB) h[e] = lgo[e];
+    __syncthreads();
+    // 3. stable scatter, 256 pairs at a time in pair order
+    for (int sub = 0; sub < pairs; sub += TPB) {
+        const int p = sub + threadIdx.x;
+        const int32_t e = p < pairs ? ids[p] : -1;
+        const bool valid = e >= 0 && e < E;
+        eid[threadIdx.x] = valid ? e : -1;
+        __syncthreads();
+        int32_t rank = 0, tot = 0, pos = -1;
+        if (valid) {
+            for (int j = 0; j < TPB; ++j) {
+                const bool same = eid[j] == e;
+                rank += (same && j < (int)threadIdx.x) ? 1 : 0;
+                tot += same ? 1 : 0;
+            }
+            pos = h[e] + rank;
+        }
+        __syncthreads();  // every pair read h[] before it moves on
+        if (valid && rank == tot - 1) h[e] += tot;
+        if (p < pairs) {
+            if (valid) {
+                order[pos] = p;
+                cpos[p] = pos;
+                prow[p] = lgpo[e] + (pos - lgo[e]);
+            } else {
+                cpos[p] = -1;
+                prow[p] = -1;
+            }
+        }
+        __syncthreads();  // eid[] and h[] are reused by the next 256 pairs
+    }
+    // 4. block -> expert: the last expert whose padded start is <= bx*128
+    for (int bx = threadIdx.x; bx < M; bx += TPB) {
+        const int64_t t = (int64_t)bx * kBlockM;
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if ((int64_t)lgpo[mid] <= t)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        gidx[bx] = lo;
+    }
+}
+
 }  // namespace
 
 int64_t contract_chunks(int64_t pairs) { return (pairs + CHUNK - 1) / CHUNK; }
@@ -167,6 +276,11 @@ hipError_t launch_contract(const int32_t *ids, int64_t pairs, int32_t E, int32_t
                            int32_t *go, int32_t *gpo, int32_t *gidx, int32_t *order, int32_t *prow,
                            int32_t *cpos, int32_t *bad, int32_t *ws, hipStream_t s) {
     const int64_t nch = contract_chunks(pairs);
+    if (nch <= 1 && E <= SMALL_E) {
+        hipLaunchKernelGGL(small_contract_kernel, dim3(1), dim3(TPB), 0, s, ids, (int32_t)pairs, E, M, gs,
+                           go, gpo, gidx, order, prow, cpos, bad);
+        return hipGetLastError();
+    }
     int32_t *cc = ws;                // [nch][E]
     int32_t *bad_c = ws + nch * E;   // [nch]
     const size_t lds = (size_t)(E + 1) * sizeof(int32_t);

@@ -53,6 +53,9 @@ def test_device_contract_workloads(name):
     (700, 8, 256, 6),      # many experts, many of them empty
     (5000, 3, 300, 7),     # E above one workgroup of scan threads
     (3, 2, 8192, 8),       # the largest supported E
+    (1024, 2, 16, 9),      # exactly one chunk: the one-launch path at its pair limit
+    (1000, 2, 1024, 10),   # the one-launch path at its expert limit
+    (1000, 2, 1025, 11),   # one chunk, one expert more: the multi-launch path
 ])
 def test_device_contract_random(T, k, E, seed):
     rng = np.random.default_rng(seed)
@@ -71,6 +74,25 @@ def test_device_contract_counts(counts):
     ids = workloads.routing_from_counts(counts, seed=11)
     print(f"device contract: counts {counts}", flush=True)
     _assert_same(_device(ids, len(counts)), C.build_contract(ids.tolist(), len(counts)))
+
+
+@pytest.mark.parametrize("T,k,E", [(64, 2, 8), (3000, 3, 40)])  # one-launch and chunked paths
+def test_device_contract_reuses_out(T, k, E):
+    """out=: the same tensors are filled again for new ids, with the new
+    tables; a dict of another shape is refused before anything runs."""
+    print(f"device contract: out= reuse T={T} k={k} E={E}", flush=True)
+    rng = np.random.default_rng(31)
+    first, second = (np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+                     for _ in range(2))
+    d1 = R.build_contract_device(torch.from_numpy(first).cuda(), E)
+    keep = {key: d1[key].data_ptr() for key in KEYS}
+    d2 = R.build_contract_device(torch.from_numpy(second).cuda(), E, out=d1)
+    torch.cuda.synchronize()
+    assert d2 is d1 and all(d2[key].data_ptr() == keep[key] for key in KEYS)
+    got = {key: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for key, v in d2.items()}
+    _assert_same(got, C.build_contract(second.tolist(), E))
+    with pytest.raises(ValueError):
+        R.build_contract_device(torch.from_numpy(second[:-1]).cuda(), E, out=d1)
 
 
 def test_device_contract_out_of_range_ids():
