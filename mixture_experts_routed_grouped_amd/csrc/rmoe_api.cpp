@@ -16,13 +16,13 @@ constexpr int64_t B = RMOE_BLOCK_M;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-constexpr int32_t kMaxDeviceExperts = 8192;
+constexpr int32_t kMaxDeviceExperts = 8192;  // the device contract keeps per-expert tables in LDS
 #ifndef RMOE_STREAM_MAX_ROWS
 #define RMOE_STREAM_MAX_ROWS 32  // average rows per expert up to which AUTO streams
 #endif
 // default bound on how long a fused down tile waits for its pair's hidden
 // rows (the longest real wait is one gate/up stage: milliseconds)
-constexpr int64_t kFusedWaitUs = 2000000;  // the device contract keeps per-expert tables in LDS
+constexpr int64_t kFusedWaitUs = 2000000;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
