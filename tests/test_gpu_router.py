@@ -54,6 +54,7 @@ def _check_router(ids, vals, x16, w16, k):
     (5, 1, 1, 128, 7),          # a single expert
     (65, 32, 32, 64, 8),        # k = E, one K chunk
     (65, 33, 32, 64, 9),        # k at its maximum, E one past a tile
+    (40001, 16, 2, 128, 10),    # enough tokens for 64-token workgroups (two per CU), ragged
 ])
 def test_router_parity(T, E, k, H, seed):
     cfg = workloads.Config("rt", T, E, k, H, 128, seed=seed)
