@@ -7,11 +7,15 @@ synthetic, already packed, HBM-resident inputs with prebuilt tables -- the
 ("MetaX-TileLang工具链", section 1.12.2).  Contract building, packing and
 allocation are outside the timed region.
 
-Prints ONE JSON line.  value = useful TFLOP/s = 6*pairs*H*I / step time.
-roofline: the dominant kernel (gate/up) against HBM (decode-shaped) or
-dense fp16 MFMA (prefill-shaped) peak, its launch duration measured with HIP
-events recorded on the stream the kernels run on.  cpu_baseline: the oracle
-timed on the host cores on a bounded sample of rows of the same workload.
+Prints ONE JSON line.  The headline workload is the large one (16384 tokens,
+E=128, top_k=8, Zipf 1.2, H=7168, I=2048: the largest that fits one GPU);
+value = useful TFLOP/s = 6*pairs*H*I / step time.  roofline: the dominant
+kernel (gate/up) against HBM (decode-shaped) or dense fp16 MFMA
+(prefill-shaped) peak, its launch duration measured with HIP events
+recorded on the stream the kernels run on.  cpu_baseline: the oracle timed
+on the host cores on a bounded sample of rows of the same workload.  The
+other workloads (decode, prefill, fine) are timed in the same run under
+"other_workloads".
 """
 from __future__ import annotations
 
@@ -40,8 +44,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode",
-                    help="tiny | decode | prefill | fine | large (default: decode)")
+    ap.add_argument("--config", default="large",
+                    help="tiny | decode | prefill | fine | large (default: large, the largest "
+                         "workload that fits one GPU)")
+    ap.add_argument("--also", default="decode,prefill,fine",
+                    help="comma-separated workloads also timed in the same run (extra keys)")
+    ap.add_argument("--also-steps", type=int, default=30)
+    ap.add_argument("--no-aux", action="store_true",
+                    help="skip the timings of the steps around the routed kernels")
     ap.add_argument("--variant", default="auto", choices=["auto", "stream", "tile"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -128,7 +138,7 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
         R.pack(inp.x, r_w.reshape(-1), c["padded_row_of_pair"], c["compact_pos_of_pair"], stacked,
                w_compact)
         R.gate_up(stacked, inp.wg, inp.wu, c["group_sizes"], c["group_padded_offsets"],
-                  c["group_idx_for_bx"], hid, variant=variant)
+                  c["group_idx_for_bx"], hid, c["pairs"], variant=variant)
         R.down(hid, inp.wd, w_compact, c["group_sizes"], c["group_offsets"],
                c["group_padded_offsets"], c["group_idx_for_bx"], out, variant=variant)
         R.combine(out, c["padded_row_of_pair"], cfg.top_k, y)
@@ -179,27 +189,35 @@ def traffic_for(kernel: str, workload: str, variant: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, target_s):
+def cpu_baseline(cfg, inp, c, target_s):
     """Time the oracle (as it stands) on a bounded sample of rows of the same
     workload, on every host core OpenMP gets; scale to TFLOP/s of useful
-    work."""
+    work.  The sample takes routed rows in expert-sorted order from at most
+    four experts spread over the routing (so at most four experts' weights
+    are copied to the host), as many as fit about target_s of oracle time."""
     import numpy as np
     from oracle import ref
     nt = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     k = cfg.top_k
     ids = inp.topk_ids
-    # sample: pairs spread over the routing, in pair order
-    pairs_all = np.arange(ids.size)
-    experts = sorted({int(e) for e in ids.reshape(-1)[:64]})
-    host = {}
+    gs, go = np.asarray(c["group_sizes"]), np.asarray(c["group_offsets"])
+    order = np.asarray(c["order"])
+    live = [int(e) for e in np.nonzero(gs)[0]]
+    experts = sorted({live[int(i)] for i in np.linspace(0, len(live) - 1, min(4, len(live)))})
+    # round robin over the chosen experts, each in its compact order
+    cand, r = [], 0
+    while len(cand) < ids.size and any(r < gs[e] for e in experts):
+        cand += [int(order[go[e] + r]) for e in experts if r < gs[e]]
+        r += 1
+    x_host = inp.x.cpu().numpy()
+    host = {e: (inp.wg[e].cpu().numpy(), inp.wu[e].cpu().numpy(), inp.wd[e].cpu().numpy())
+            for e in experts}
 
     def rows_for(sel):
         xs, gl, ul, dl, ws = [], [], [], [], []
         for p in sel:
             t, j = divmod(int(p), k)
             e = int(ids[t][j])
-            if e not in host:
-                host[e] = (inp.wg[e].cpu().numpy(), inp.wu[e].cpu().numpy(), inp.wd[e].cpu().numpy())
             xs.append(x_host[t])
             gl.append(host[e][0])
             ul.append(host[e][1])
@@ -207,46 +225,34 @@ def cpu_baseline(cfg, inp, target_s):
             ws.append(float(inp.topk_w[t][j]))
         return xs, gl, ul, dl, ws
 
-    x_host = inp.x.cpu().numpy()
     # calibrate with one row per thread, then size the sample to ~target_s
-    sel = pairs_all[:nt]
-    args = rows_for(sel)
+    args = rows_for(cand[:nt])
     t0 = time.perf_counter()
     ref.moe_rows(*args, n_threads=nt)
     t_cal = time.perf_counter() - t0
     n_rounds = max(1, int(target_s / max(t_cal, 1e-6)))
-    n_rows = min(len(pairs_all), nt * n_rounds)
-    sel = pairs_all[:n_rows]
-    args = rows_for(sel)
+    n_rows = min(len(cand), nt * n_rounds)
+    args = rows_for(cand[:n_rows])
     t0 = time.perf_counter()
     ref.moe_rows(*args, n_threads=nt)
     dt = time.perf_counter() - t0
     flops = 6.0 * n_rows * cfg.hidden * cfg.intermediate
-    del experts
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nt, "kind": "oracle",
-            "sample": f"{n_rows} of {ids.size} routed rows (first in pair order), full H and I; "
-                      f"{dt:.2f} s wall"}
+            "sample": f"{n_rows} of {ids.size} routed rows, taken in turn from experts "
+                      f"{experts} in expert-sorted order, full H and I; {dt:.2f} s wall"}
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib, args.steps)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(expert or tensor sharding is described, not implemented). Run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def measure(cfg, variant, steps, warmup, with_aux=False):
+    """Inputs of one workload resident on the GPU, prebuilt tables, then
+    `warmup` untimed and `steps` timed forwards (gate/up and down launches,
+    HIP events recorded around each on the stream they run on)."""
     import numpy as np
     import torch
 
     import mixture_experts_routed_grouped_amd as R
     import workloads
 
-    cfg = workloads.CONFIGS[args.config]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     inp = workloads.make_inputs(cfg, device=dev)
     c = R.build_contract(inp.topk_ids, cfg.experts)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
@@ -260,37 +266,35 @@ def main():
     R.pack(inp.x, topk_w, prow, cpos, stacked, w_compact)
     hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
     out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
-    variant = args.variant
-    # the library's automatic choice (pick_variant): streaming up to 32 rows per expert
-    resolved = variant if variant != "auto" else ("stream" if c["pairs"] <= 32 * E else "tile")
+    # the family the library runs for this batch (its own choice, asked through the C-ABI)
+    resolved = R.pick_variant(c["pairs"], E, variant)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        R.gate_up(stacked, inp.wg, inp.wu, gs, gpo, gidx, hid, variant=resolved)
+        R.gate_up(stacked, inp.wg, inp.wu, gs, gpo, gidx, hid, c["pairs"], variant=resolved)
         if evs is not None:
             evs[1].record()
         R.down(hid, inp.wd, w_compact, gs, go, gpo, gidx, out, variant=resolved)
         if evs is not None:
             evs[2].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     alg = algorithmic(cfg, c, resolved)
-    useful = cfg.useful_flops()
-    value = useful / (ms_per_step * 1e-3) / 1e12
+    value = cfg.useful_flops() / (ms_per_step * 1e-3) / 1e12
     gu_s = statistics.fmean(gu_ms) * 1e-3
     dn_s = statistics.fmean(dn_ms) * 1e-3
     hbm_bound = resolved == "stream"
@@ -306,12 +310,12 @@ def main():
                                     else "tile_kernel<true> (256x256 LDS-tiled MFMA)")
     roof["traffic"] = traffic_for("gate_up", cfg.name, resolved)
     total_bytes = alg["gate_up"]["bytes"] + alg["down"]["bytes"]
-    result = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+    res = {
+        "value": value, "ms_per_step": ms_per_step,
         "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens, E={E}, top_k={cfg.top_k}, "
-                               f"H={H}, I={I}, {cfg.routing} routing, seed {cfg.seed}",
+                               f"H={H}, I={I}, {cfg.routing} routing"
+                               + (f" s={cfg.zipf_s}" if cfg.routing == "zipf" else "")
+                               + f", seed {cfg.seed}",
                    "tokens": cfg.tokens, "experts": E, "top_k": cfg.top_k, "hidden": H,
                    "intermediate": I, "pairs": c["pairs"], "num_blocks_m": c["num_blocks_m"],
                    "experts_active": alg["experts_active"], "scope": "routed_kernel_only",
@@ -329,13 +333,58 @@ def main():
                      "tflops": alg["down"]["flops"] / dn_s / 1e12},
         },
         "latency_ms": stats_ms(step_ms),
-        "device": torch.cuda.get_device_name(0),
     }
-    result["aux_kernels_us"] = aux_timings(cfg, inp, hid, out, resolved)
+    if with_aux:
+        res["aux_kernels_us"] = aux_timings(cfg, inp, hid, out, resolved)
+    return res, inp, c
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib, args.steps)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(expert or tensor sharding is described, not implemented). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads
+
+    torch.cuda.set_device(0)
+    cfg = workloads.CONFIGS[args.config]
+    head, inp, c = measure(cfg, args.variant, args.steps, args.warmup, with_aux=not args.no_aux)
+    result = {
+        "metric": METRIC, "value": head.pop("value"), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic", "config": head.pop("config"), "roofline": head.pop("roofline"),
+    }
+    result.update(head)
+    result["device"] = torch.cuda.get_device_name(0)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, c, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    del inp
+    torch.cuda.empty_cache()
+    # the other workloads, same protocol, fewer steps: each one's step time,
+    # useful TFLOP/s and the gate/up kernel's roofline
+    also = {}
+    for name in [w for w in args.also.split(",") if w and w != cfg.name]:
+        r, inp_o, _ = measure(workloads.CONFIGS[name], args.variant, args.also_steps,
+                              max(2, args.warmup // 2))
+        also[name] = {"value": r["value"], "ms_per_step": r["ms_per_step"],
+                      "steps": args.also_steps, "workload": r["config"]["workload"],
+                      "variant": r["config"]["variant"], "roofline": r["roofline"],
+                      "step_mfma_frac": r["step_mfma_frac"], "step_hbm_frac": r["step_hbm_frac"],
+                      "kernels_us": {k: v["avg_us"] for k, v in r["kernels"].items()}}
+        del inp_o
+        torch.cuda.empty_cache()
+    if also:
+        result["other_workloads"] = also
     print(json.dumps(result), flush=True)
 
 

@@ -16,7 +16,12 @@
  * c = group_offsets[e] + token_offset + i (section 实现要点: tokens, the
  * workspace and out use padded rows, routed weights use compact rows).
  * Rows i >= actual_rows (padding) are neither computed nor written, in out
- * and in the workspace alike.
+ * and in the workspace alike.  A block is computed only if its table entry
+ * e lies in [0, E) and names the expert whose padded interval
+ * [group_padded_offsets[e], group_padded_offsets[e+1]) holds row bx*128 --
+ * always so for tables that satisfy the contract; a corrupted entry leaves
+ * that block's rows unwritten in both kernel families alike
+ * (rmoe_validate_contract_device reports it).
  *
  * Conventions for every entry point:
  *   - Return 0 (RMOE_OK) on success, a negative rmoe_status otherwise; no
@@ -106,8 +111,62 @@ RMOE_API int rmoe_validate_contract(const int32_t *group_sizes, const int32_t *g
                                     int32_t num_blocks_m, int64_t total_padded_tokens,
                                     int64_t total_valid_tokens);
 
-/* Bytes of the fp16 hidden workspace: total_padded_tokens * intermediate * 2. */
+/*
+ * The same rules checked on DEVICE copies of the tables, asynchronously on
+ * `stream` (one small launch, no host read-back): *violations (one int32,
+ * device, caller-owned) receives the number of violated rule instances --
+ * 0 for valid tables.  Rules on sizes alone (num_blocks_m = ceil(pairs/128)
+ * + E, num_blocks_m*128 <= total_padded_tokens) are checked synchronously
+ * and return RMOE_ERR_CONTRACT.  The forward kernels themselves compute a
+ * block only when group_idx_for_bx maps it to the expert whose padded
+ * interval holds it, so a corrupted table leaves rows unwritten instead of
+ * reading out of bounds; this call is how to find out.
+ * Errors: RMOE_ERR_INVALID_ARGUMENT, RMOE_ERR_MISALIGNED (4-byte),
+ * RMOE_ERR_CONTRACT, RMOE_ERR_LAUNCH.
+ */
+RMOE_API int rmoe_validate_contract_device(const int32_t *group_sizes,
+                                           const int32_t *group_offsets,
+                                           const int32_t *group_padded_offsets,
+                                           const int32_t *group_idx_for_bx, int32_t num_experts,
+                                           int32_t num_blocks_m, int64_t total_padded_tokens,
+                                           int64_t total_valid_tokens, int32_t *violations,
+                                           void *stream);
+
+/*
+ * Bytes of the fp16 hidden workspace: total_padded_tokens * intermediate * 2.
+ * It is the kernel's global intermediate up_logits of shape
+ * [total_padded_tokens, intermediate] in fp16 ("Fused MoE GEMM 提交说明",
+ * 完整算子代码: the Step-1 grid writes it, the Step-2 grid reads it).
+ * Returns 0 for non-positive sizes.
+ */
 RMOE_API size_t rmoe_workspace_bytes(int64_t total_padded_tokens, int64_t intermediate);
+
+/*
+ * Sizes of the contract for num_pairs (token, expert) pairs over
+ * num_experts experts ("moe_dispatch_contract.py", build_contract step 4):
+ *   *num_blocks_m = ceil(num_pairs / 128) + num_experts, the number of
+ *   128-row blocks the grid covers (each expert owns at most one partly
+ *   filled block plus its slack, so the padded intervals always fit);
+ *   *total_padded_tokens = 128 * *num_blocks_m, the row count of the padded
+ *   token, workspace and out matrices (a caller may use more rows).
+ * Either output may be NULL.  Host only, no GPU work.
+ * Errors: RMOE_ERR_INVALID_ARGUMENT for negative pairs, num_experts < 1, or
+ * sizes whose padded row count would not fit int32.
+ */
+RMOE_API int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t *num_blocks_m,
+                                 int64_t *total_padded_tokens);
+
+/*
+ * The kernel family the forward, rmoe_gate_up_f16 and rmoe_down_f16 run for
+ * a batch: `variant` itself if it is RMOE_VARIANT_STREAM or _TILE, else
+ * (RMOE_VARIANT_AUTO) the choice from num_pairs and num_experts alone --
+ * the same function every entry point calls, so the two stages of one batch
+ * always agree.  AUTO streams while the batch averages at most 32 routed
+ * rows per expert (there an expert's GEMM is bound by reading its weights,
+ * as the contract tutorial's closing note says of small M) and tiles above.
+ * Returns RMOE_VARIANT_STREAM or RMOE_VARIANT_TILE, or a negative status.
+ */
+RMOE_API int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts);
 
 /*
  * The fused expert FFN forward (the submission's run_kernel, with the
@@ -190,15 +249,18 @@ RMOE_API int rmoe_forward_fused_f16(const void *stacked_expert_tokens, const voi
 
 /*
  * Stage 1 alone (the Step-1 grid of section 完整算子代码): workspace rows =
- * fp16(silu(x.Wg^T) * (x.Wu^T)) for valid rows.  Arguments as above.
+ * fp16(silu(x.Wg^T) * (x.Wu^T)) for valid rows.  Arguments as above;
+ * total_valid_tokens (the pair count, group_offsets[E]) only feeds the
+ * family choice, which is rmoe_pick_variant's and so the same as
+ * rmoe_down_f16's for the same batch.
  */
 RMOE_API int rmoe_gate_up_f16(const void *stacked_expert_tokens, const void *gate_w,
                               const void *up_w, const int32_t *group_sizes,
                               const int32_t *group_padded_offsets,
                               const int32_t *group_idx_for_bx, void *workspace, int64_t hidden,
                               int64_t intermediate, int32_t num_experts,
-                              int64_t total_padded_tokens, int32_t num_blocks_m,
-                              int32_t variant, void *stream);
+                              int64_t total_padded_tokens, int64_t total_valid_tokens,
+                              int32_t num_blocks_m, int32_t variant, void *stream);
 
 /*
  * Stage 2 alone (the Step-2 grid): out rows = fp16((hidden.Wd^T) * w[c])

@@ -21,9 +21,9 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librmoe.so")
 
-BLOCK_M = 128
 VARIANT_AUTO, VARIANT_STREAM, VARIANT_TILE = 0, 1, 2
 _VARIANTS = {"auto": 0, "stream": 1, "tile": 2, 0: 0, 1: 1, 2: 2}
+_VARIANT_NAMES = {VARIANT_STREAM: "stream", VARIANT_TILE: "tile"}
 
 
 class RmoeError(RuntimeError):
@@ -41,13 +41,16 @@ _SIGS = {
     "rmoe_version": ([], ctypes.c_char_p),
     "rmoe_build_contract": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P], ctypes.c_int),
     "rmoe_validate_contract": ([_P, _P, _P, _P, _I32, _I32, _I64, _I64], ctypes.c_int),
+    "rmoe_validate_contract_device": ([_P, _P, _P, _P, _I32, _I32, _I64, _I64, _P, _P], ctypes.c_int),
     "rmoe_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "rmoe_contract_sizes": ([_I64, _I32, _P, _P], ctypes.c_int),
+    "rmoe_pick_variant": ([_I32, _I64, _I32], ctypes.c_int),
     "rmoe_forward_f16": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
     "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
                                  ctypes.c_int),
     "rmoe_fused_sync_words": ([_I32], ctypes.c_size_t),
     "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
-    "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I32, _I32, _P], ctypes.c_int),
+    "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
     "rmoe_combine_f16": ([_P, _P, _I64, _I32, _I64, _P, _I64, _P], ctypes.c_int),
@@ -97,7 +100,7 @@ def build_contract(topk_ids, num_experts: int) -> dict:
     T, k = ids.shape
     E = int(num_experts)
     pairs = T * k
-    M_cap = -(-pairs // BLOCK_M) + E
+    M_cap, Tp = contract_sizes(pairs, E)
     gs = np.zeros(E, np.int32)
     go = np.zeros(E + 1, np.int32)
     gpo = np.zeros(E + 1, np.int32)
@@ -122,7 +125,7 @@ def build_contract(topk_ids, num_experts: int) -> dict:
         "order": order[:pairs].copy(),
         "padded_row_of_pair": prow[:pairs].copy(),
         "compact_pos_of_pair": cpos[:pairs].copy(),
-        "total_padded_tokens": M * BLOCK_M,
+        "total_padded_tokens": Tp,
     }
 
 
@@ -136,8 +139,46 @@ def validate_contract(group_sizes, group_offsets, group_padded_offsets, group_id
                                             int(total_valid_tokens)))
 
 
+def validate_contract_device(group_sizes, group_offsets, group_padded_offsets, group_idx_for_bx,
+                             total_padded_tokens, total_valid_tokens, violations=None, stream=None):
+    """Enqueue the contract check on device tables (rmoe_validate_contract_device);
+    returns the device int32 tensor [1] that receives the violation count
+    (0: valid).  Rules on sizes alone raise RmoeError at once."""
+    torch = _torch()
+    i32 = torch.int32
+    E = group_sizes.numel()
+    if violations is None:
+        violations = torch.empty(1, dtype=i32, device=group_sizes.device)
+    st = lib().rmoe_validate_contract_device(
+        _dev(group_sizes, i32, "group_sizes"), _dev(group_offsets, i32, "group_offsets"),
+        _dev(group_padded_offsets, i32, "group_padded_offsets"),
+        _dev(group_idx_for_bx, i32, "group_idx_for_bx"), E, group_idx_for_bx.numel(),
+        int(total_padded_tokens), int(total_valid_tokens), _dev(violations, i32, "violations"),
+        _stream(group_sizes, stream))
+    _check(st, "rmoe_validate_contract_device")
+    return violations
+
+
 def workspace_bytes(total_padded_tokens: int, intermediate: int) -> int:
     return int(lib().rmoe_workspace_bytes(int(total_padded_tokens), int(intermediate)))
+
+
+def contract_sizes(num_pairs: int, num_experts: int) -> tuple[int, int]:
+    """(num_blocks_m, total_padded_tokens) of the contract for a batch, from
+    the library (rmoe_contract_sizes)."""
+    m = ctypes.c_int32(0)
+    tp = ctypes.c_int64(0)
+    _check(lib().rmoe_contract_sizes(int(num_pairs), int(num_experts), ctypes.byref(m),
+                                     ctypes.byref(tp)), "rmoe_contract_sizes")
+    return int(m.value), int(tp.value)
+
+
+def pick_variant(num_pairs: int, num_experts: int, variant="auto") -> str:
+    """The kernel family ("stream" or "tile") the library runs for a batch
+    (rmoe_pick_variant: the choice every forward and stage entry makes)."""
+    v = int(lib().rmoe_pick_variant(_VARIANTS[variant], int(num_pairs), int(num_experts)))
+    _check(min(v, 0), "rmoe_pick_variant")
+    return _VARIANT_NAMES[v]
 
 
 # ------------------------------------------------------------- device calls
@@ -207,12 +248,17 @@ def fused_sync_words(num_blocks_m: int) -> int:
     return int(lib().rmoe_fused_sync_words(int(num_blocks_m)))
 
 
-def fused_sync(device, num_blocks_m: int):
-    """A zeroed int32 sync buffer for forward_fused, cached per (device,
-    size); the kernel leaves it zero after each completed call."""
+def fused_sync(device, num_blocks_m: int, stream=None):
+    """A zeroed int32 sync buffer for forward_fused, cached per (device, size,
+    stream): calls on one stream run one after another and may share it,
+    calls on different streams get different buffers.  The kernel leaves it
+    zero after each completed call, except the sticky error word."""
     torch = _torch()
     device = torch.device(device)
-    key = (device.index or 0, fused_sync_words(num_blocks_m))
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    key = (device.index or 0, fused_sync_words(num_blocks_m), handle)
     buf = _SYNC.get(key)
     if buf is None:
         buf = torch.zeros(key[1], dtype=torch.int32, device=device)
@@ -220,14 +266,30 @@ def fused_sync(device, num_blocks_m: int):
     return buf
 
 
+def fused_sync_errors(sync, clear: bool = True) -> int:
+    """Tiles the single-launch forwards on ``sync`` skipped because a wait
+    for hidden rows timed out (their out rows are then unwritten); 0 in
+    normal operation.  Waits for the device (it reads the word back), so
+    call it when a result is about to be used; ``clear`` resets the count."""
+    torch = _torch()
+    torch.cuda.synchronize(sync.device)
+    n = int(sync[FUSED_SYNC_ERROR].item())
+    if clear and n:
+        sync[FUSED_SYNC_ERROR] = 0
+        torch.cuda.synchronize(sync.device)
+    return n
+
+
 def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
                   group_offsets, group_padded_offsets, group_idx_for_bx, workspace, out, sync=None,
                   max_wait_us=0, stream=None):
     """Both stages in one launch (rmoe_forward_fused_f16): same arguments and
     results as forward(..., variant="tile"); ``sync`` is the int32 queue
-    state (default: a cached zeroed buffer; calls sharing one must not
-    overlap in time); ``max_wait_us`` bounds a down tile's wait for its
-    hidden rows (0: the library's default)."""
+    state (default: a zeroed buffer cached per device, size and stream;
+    calls sharing one must not overlap in time); ``max_wait_us`` bounds a
+    down tile's wait for its hidden rows (0: the library's default).  A wait
+    that times out skips its tile and counts it in the sync buffer's error
+    word: check it with ``fused_sync_errors(sync)`` before using ``out``."""
     torch = _torch()
     x = stacked_expert_tokens
     E, I, H = gate_w.shape
@@ -242,7 +304,7 @@ def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_wei
         raise ValueError("group tables must have E, E+1, E+1 entries")
     M = group_idx_for_bx.numel()
     if sync is None:
-        sync = fused_sync(x.device, M)
+        sync = fused_sync(x.device, M, stream)
     if sync.numel() < fused_sync_words(M):
         raise ValueError("sync buffer too small")
     f16, i32 = torch.float16, torch.int32
@@ -259,8 +321,9 @@ def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_wei
 
 
 def gate_up(stacked_expert_tokens, gate_w, up_w, group_sizes, group_padded_offsets,
-            group_idx_for_bx, workspace, variant="auto", stream=None):
-    """Stage 1 alone: workspace = fp16(silu(x Wg^T) * (x Wu^T)) on valid rows."""
+            group_idx_for_bx, workspace, num_pairs, variant="auto", stream=None):
+    """Stage 1 alone: workspace = fp16(silu(x Wg^T) * (x Wu^T)) on valid rows.
+    ``num_pairs`` (routed rows, group_offsets[E]) feeds the family choice."""
     torch = _torch()
     x = stacked_expert_tokens
     E, I, H = gate_w.shape
@@ -270,7 +333,8 @@ def gate_up(stacked_expert_tokens, gate_w, up_w, group_sizes, group_padded_offse
         _dev(up_w, f16, "up_w"), _dev(group_sizes, i32, "group_sizes"),
         _dev(group_padded_offsets, i32, "group_padded_offsets"),
         _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
-        H, I, E, x.shape[0], group_idx_for_bx.numel(), _VARIANTS[variant], _stream(x, stream))
+        H, I, E, x.shape[0], int(num_pairs), group_idx_for_bx.numel(), _VARIANTS[variant],
+        _stream(x, stream))
     _check(st, "rmoe_gate_up_f16")
 
 
@@ -359,7 +423,7 @@ def build_contract_device(topk_ids, num_experts: int, stream=None, out=None) -> 
         raise ValueError("topk_ids must be [T, k]")
     T, k = topk_ids.shape
     pairs, E = T * k, int(num_experts)
-    M = -(-pairs // BLOCK_M) + E
+    M, Tp = contract_sizes(pairs, E)
     dev = topk_ids.device
     nbytes = contract_workspace_bytes(pairs, E)
     if nbytes == 0:
@@ -385,7 +449,7 @@ def build_contract_device(topk_ids, num_experts: int, stream=None, out=None) -> 
         ptr(out["bad_ids"]), ptr(ws), nbytes, _stream(topk_ids, stream))
     _check(st, "rmoe_build_contract_device")
     out["_workspace"] = ws  # keeps the scratch alive until the stream has used it
-    out.update(num_blocks_m=nb.value, total_padded_tokens=BLOCK_M * nb.value, pairs=pairs)
+    out.update(num_blocks_m=nb.value, total_padded_tokens=Tp, pairs=pairs)
     return out
 
 

@@ -209,24 +209,58 @@ size_t rmoe_workspace_bytes(int64_t total_padded_tokens, int64_t intermediate) {
     return (size_t)total_padded_tokens * (size_t)intermediate * 2u;
 }
 
+int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t *num_blocks_m,
+                        int64_t *total_padded_tokens) {
+    if (num_pairs < 0 || num_experts < 1 || num_pairs > INT32_MAX / 2)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    const int64_t M = ceil_div(num_pairs, B) + num_experts;
+    if (M * B > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
+    if (num_blocks_m) *num_blocks_m = (int32_t)M;
+    if (total_padded_tokens) *total_padded_tokens = M * B;
+    return RMOE_OK;
+}
+
+int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts) {
+    if (bad_variant(variant) || num_pairs < 0 || num_experts < 1) return RMOE_ERR_INVALID_ARGUMENT;
+    return pick_variant(variant, num_pairs, num_experts);
+}
+
+int rmoe_validate_contract_device(const int32_t *gs, const int32_t *go, const int32_t *gpo,
+                                  const int32_t *gidx, int32_t num_experts, int32_t num_blocks_m,
+                                  int64_t total_padded_tokens, int64_t total_valid_tokens,
+                                  int32_t *violations, void *stream) {
+    if (!gs || !go || !gpo || !violations || num_experts < 1 || num_blocks_m < 0 ||
+        total_valid_tokens < 0 || (num_blocks_m > 0 && !gidx))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (!aligned4(gs) || !aligned4(go) || !aligned4(gpo) || !aligned4(gidx) || !aligned4(violations))
+        return RMOE_ERR_MISALIGNED;
+    // the size rules need no table: they are checked here, synchronously
+    if (total_valid_tokens > INT32_MAX / 2 ||
+        (int64_t)num_blocks_m != ceil_div(total_valid_tokens, B) + num_experts ||
+        (int64_t)num_blocks_m * B > total_padded_tokens)
+        return RMOE_ERR_CONTRACT;
+    return to_status(rmoe::launch_validate(gs, go, gpo, gidx, num_experts, num_blocks_m,
+                                           total_valid_tokens, violations,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int rmoe_gate_up_f16(const void *x, const void *gate_w, const void *up_w, const int32_t *gs,
                      const int32_t *gpo, const int32_t *gidx, void *workspace, int64_t hidden,
                      int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
-                     int32_t num_blocks_m, int32_t variant, void *stream) {
+                     int64_t total_valid_tokens, int32_t num_blocks_m, int32_t variant,
+                     void *stream) {
     int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
     if (st != RMOE_OK) return st;
-    if (bad_variant(variant)) return RMOE_ERR_INVALID_ARGUMENT;
+    if (bad_variant(variant) || total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
     if (!x || !gate_w || !up_w || !gs || !gpo || !workspace || (num_blocks_m > 0 && !gidx))
         return RMOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(x) || !aligned16(gate_w) || !aligned16(up_w) || !aligned16(workspace) ||
         !aligned4(gs) || !aligned4(gpo) || !aligned4(gidx))
         return RMOE_ERR_MISALIGNED;
-    // without the compact offsets the average group size is unknown: the
-    // variant decides, AUTO takes the tiled family only for many blocks
-    const int64_t pairs_est = ((int64_t)num_blocks_m - num_experts) * B;
+    // the same family choice as rmoe_down_f16 and the forward for this batch
     return gate_up_impl(x, gate_w, up_w, gs, gpo, gidx, workspace, hidden, intermediate,
-                        num_experts, total_padded_tokens, num_blocks_m, pairs_est, variant,
-                        stream);
+                        num_experts, total_padded_tokens, num_blocks_m, total_valid_tokens,
+                        variant, stream);
 }
 
 int rmoe_down_f16(const void *workspace, const void *down_w, const float *rw, const int32_t *gs,

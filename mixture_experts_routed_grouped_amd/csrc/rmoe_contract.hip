@@ -268,7 +268,60 @@ __global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__re
     }
 }
 
+// The contract's rules on device tables ("moe_dispatch_contract.py", the
+// three self-checks in their strict form), counted: offsets start at 0 and
+// step by the group sizes, each padded span is (size/128 + 1)*128, the
+// compact total is the pair count, the padded total fits in M blocks, and
+// every block maps to the last expert whose padded start is <= bx*128.
+// One workgroup; each violated rule instance adds 1.
+__global__ __launch_bounds__(TPB) void validate_kernel(const int32_t *__restrict__ gs,
+                                                       const int32_t *__restrict__ go,
+                                                       const int32_t *__restrict__ gpo,
+                                                       const int32_t *__restrict__ gidx, int32_t E,
+                                                       int32_t M, int64_t pairs,
+                                                       int32_t *__restrict__ violations) {
+    __shared__ int32_t bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    int32_t mine = 0;
+    if (threadIdx.x == 0) {
+        mine += go[0] != 0;
+        mine += gpo[0] != 0;
+        mine += (int64_t)go[E] != pairs;
+        mine += (int64_t)gpo[E] > (int64_t)M * kBlockM;
+    }
+    for (int e = threadIdx.x; e < E; e += TPB) {
+        const int64_t c = gs[e];
+        mine += c < 0;
+        mine += (int64_t)go[e + 1] - go[e] != c;
+        mine += (int64_t)gpo[e + 1] - gpo[e] != (c / kBlockM + 1) * kBlockM;
+    }
+    for (int bx = threadIdx.x; bx < M; bx += TPB) {
+        const int64_t t = (int64_t)bx * kBlockM;
+        int lo = 0, hi = E - 1;  // stays in [0, E) whatever gpo holds
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if ((int64_t)gpo[mid] <= t)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        mine += gidx[bx] != lo;
+    }
+    if (mine) atomicAdd(&bad, mine);
+    __syncthreads();
+    if (threadIdx.x == 0) *violations = bad;
+}
+
 }  // namespace
+
+hipError_t launch_validate(const int32_t *gs, const int32_t *go, const int32_t *gpo,
+                           const int32_t *gidx, int32_t E, int32_t M, int64_t pairs,
+                           int32_t *violations, hipStream_t s) {
+    hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(TPB), 0, s, gs, go, gpo, gidx, E, M, pairs,
+                       violations);
+    return hipGetLastError();
+}
 
 int64_t contract_chunks(int64_t pairs) { return (pairs + CHUNK - 1) / CHUNK; }
 

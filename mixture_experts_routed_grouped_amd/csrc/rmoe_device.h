@@ -23,12 +23,24 @@ struct BlockInfo {
     int rows;          // valid rows in [0, 128]
 };
 
+// The block is computed only when group_idx_for_bx names the expert whose
+// padded interval [gpo[e], gpo[e+1]) holds it; a table entry that names any
+// other expert (or none) leaves the block's rows unwritten.  With a valid
+// table this changes nothing; with a corrupted one both kernel families
+// skip exactly the same blocks (the tiled family checks each block of its
+// work items against the table the same way), and no read leaves the
+// tables or the expert's rows.
 __device__ __forceinline__ BlockInfo block_info(const int32_t *__restrict__ gs,
                                                 const int32_t *__restrict__ gpo,
-                                                const int32_t *__restrict__ gidx, int bx) {
+                                                const int32_t *__restrict__ gidx, int E, int bx) {
     BlockInfo b;
     b.e = gidx[bx];
-    b.token_offset = bx * kBlockM - gpo[b.e];
+    b.rows = 0;
+    b.token_offset = 0;
+    if (b.e < 0 || b.e >= E) return b;
+    const int start = bx * kBlockM;
+    if (start < gpo[b.e] || start >= gpo[b.e + 1]) return b;
+    b.token_offset = start - gpo[b.e];
     int r = gs[b.e] - b.token_offset;
     b.rows = r < 0 ? 0 : (r > kBlockM ? kBlockM : r);
     return b;

@@ -65,6 +65,12 @@ hipError_t launch_combine(const _Float16 *out, const int32_t *prow, int64_t T, i
 hipError_t launch_router(const _Float16 *x, const _Float16 *w, int64_t T, int64_t H, int32_t E,
                          int32_t k, int32_t *ids, float *vals, hipStream_t s);
 
+// Device-side check of the contract tables: writes the number of violated
+// rules to *violations (one workgroup, no memset needed).
+hipError_t launch_validate(const int32_t *gs, const int32_t *go, const int32_t *gpo,
+                           const int32_t *gidx, int32_t E, int32_t M, int64_t pairs,
+                           int32_t *violations, hipStream_t s);
+
 // Device-side contract build.  ws holds contract_chunks(pairs) * (E + 1)
 // int32 of scratch.
 int64_t contract_chunks(int64_t pairs);

@@ -230,7 +230,7 @@ template <bool DUAL, int KS, int D, int TT>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int bx = blockIdx.y;
-    const BlockInfo bi = block_info(a.gs, a.gpo, a.gidx, bx);
+    const BlockInfo bi = block_info(a.gs, a.gpo, a.gidx, a.E, bx);
     if (bi.rows == 0) return;
     // wave-uniform by construction; readfirstlane keeps the K range and the
     // loop bounds in scalar registers (uniform branches)

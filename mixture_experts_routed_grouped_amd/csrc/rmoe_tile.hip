@@ -331,14 +331,20 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
     }
 }
 
-// Runs work item it (rmoe_sched.h) with the workgroup's LDS.
+// Runs work item it (rmoe_sched.h) with the workgroup's LDS.  The item list
+// comes from the group sizes and padded offsets; each of its blocks is
+// computed only if group_idx_for_bx maps it to the item's expert (the rule
+// the streaming family applies per block, in block_info), so both families
+// act on the same table and skip the same blocks of a corrupted one.
 template <bool DUAL, bool WT = false>
 __device__ __forceinline__ void run_item(const StageArgs &a, unsigned char *smem, const TileItem &it) {
     BlockInfo b0;
     b0.e = it.e;
     b0.token_offset = it.off;
-    b0.rows = it.rows0;
-    run_tile<DUAL, WT>(a, smem, it.nt, it.bx, b0, it.rows1 > 0, it.rows1);
+    b0.rows = a.gidx[it.bx] == it.e ? it.rows0 : 0;
+    const int rows1 = (it.rows1 > 0 && a.gidx[it.bx + 1] == it.e) ? it.rows1 : 0;
+    if (b0.rows == 0 && rows1 == 0) return;
+    run_tile<DUAL, WT>(a, smem, it.nt, it.bx, b0, rows1 > 0, rows1);
 }
 
 // Persistent kernel: one workgroup per CU (a multiple of 8 of them, LDS_BYTES

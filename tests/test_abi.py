@@ -124,7 +124,8 @@ def test_argument_errors_without_gpu():
     assert fwd(ptrs, pairs=-1) == -1
     assert fwd(ptrs, variant=7) == -1
     assert fwd([odd] + ptrs[1:]) == -3                    # misaligned fp16 tensor
-    assert L.rmoe_gate_up_f16(*([fake] * 7), 256, 100, 4, 640, 5, 0, None) == -2
+    assert L.rmoe_gate_up_f16(*([fake] * 7), 256, 100, 4, 640, 18, 5, 0, None) == -2
+    assert L.rmoe_gate_up_f16(*([fake] * 7), 256, 128, 4, 640, -1, 5, 0, None) == -1
     assert L.rmoe_down_f16(*([fake] * 8), 256, 128, 4, 640, -3, 5, 0, None) == -1
     assert L.rmoe_pack_f16(fake, fake, fake, fake, 3, 2, 12, fake, fake, 640, None) == -2
     assert L.rmoe_combine_f16(fake, fake, -1, 2, 16, fake, 640, None) == -1
@@ -201,3 +202,65 @@ def test_fused_argument_errors_without_gpu():
     assert fz(x=odd) == -3
     assert fz(sync=ctypes.c_void_p(0x10002)) == -3        # int32 words
     assert fz(M=0, Tp=0, pairs=0) == 0                    # no blocks: nothing launched
+
+
+def test_contract_sizes_and_variant_queries():
+    """rmoe_contract_sizes is build_contract step 4 ("moe_dispatch_contract.py":
+    m_blocks = ceil(pairs/128) + E) and agrees with the contract oracle's
+    block count; rmoe_pick_variant is the one family choice of every entry."""
+    for pairs, E in [(0, 1), (18, 4), (128, 8), (129, 8), (8192, 8), (49152, 64), (131072, 128)]:
+        M, Tp = R.contract_sizes(pairs, E)
+        assert M == -(-pairs // 128) + E and Tp == 128 * M
+        ids = workloads.routing_from_counts([pairs // E] * (E - 1) + [pairs - (pairs // E) * (E - 1)])
+        assert C.build_contract(ids.tolist(), E)["num_blocks_m"] == M
+    L = R.lib()
+    assert L.rmoe_contract_sizes(-1, 4, None, None) == -1
+    assert L.rmoe_contract_sizes(10, 0, None, None) == -1
+    assert L.rmoe_contract_sizes(2 ** 31, 4, None, None) == -1
+    assert L.rmoe_contract_sizes(10, 4, None, None) == 0    # outputs are optional
+    # streaming while the batch averages at most 32 rows per expert, tiles above
+    assert R.pick_variant(128, 8) == "stream"               # decode workload
+    assert R.pick_variant(256, 8) == "stream"
+    assert R.pick_variant(257, 8) == "tile"
+    assert R.pick_variant(8192, 8) == "tile"                # prefill workload
+    assert R.pick_variant(8192, 8, "stream") == "stream"
+    assert R.pick_variant(128, 8, "tile") == "tile"
+    assert L.rmoe_pick_variant(7, 10, 4) == -1
+    assert L.rmoe_pick_variant(0, -1, 4) == -1
+    assert L.rmoe_pick_variant(0, 10, 0) == -1
+
+
+def test_validate_device_argument_errors_without_gpu():
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10002)
+
+    def vd(E=4, M=5, Tp=640, pairs=18, viol=fake, gs=fake):
+        return L.rmoe_validate_contract_device(gs, fake, fake, fake, E, M, Tp, pairs, viol, None)
+
+    assert vd(viol=None) == -1
+    assert vd(gs=None) == -1
+    assert vd(E=0) == -1
+    assert vd(gs=odd) == -3
+    assert vd(M=6) == -5                                  # not ceil(18/128) + 4
+    assert vd(Tp=512) == -5                               # 5 blocks do not fit 512 rows
+    assert vd(pairs=-1) == -1
+
+
+def test_binding_holds_no_contract_arithmetic():
+    """The Python binding only marshals: block counts, padded sizes and the
+    family choice come from the library (rmoe_contract_sizes,
+    rmoe_pick_variant), so no formula of the contract is written there."""
+    import ast
+    src = open(os.path.join(ROOT, "mixture_experts_routed_grouped_amd", "__init__.py")).read()
+    tree = ast.parse(src)
+    for node in ast.walk(tree):
+        # a number 128 (the block size) or 32 (the streaming threshold)
+        # anywhere in the binding would be contract or policy arithmetic
+        if isinstance(node, ast.Constant) and node.value in (128, 32):
+            raise AssertionError(f"binding line {node.lineno}: constant {node.value}")
+        if isinstance(node, ast.Name) and "BLOCK_M" == node.id.upper():
+            raise AssertionError(f"binding line {node.lineno}: {node.id}")
+    for name in ("bench.py", "__graft_entry__.py"):
+        text = open(os.path.join(ROOT, name)).read()
+        assert "32 * E" not in text and "-(-" not in text, name

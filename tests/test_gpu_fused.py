@@ -111,6 +111,9 @@ def test_fused_full_size(name):
     sync = torch.zeros(R.fused_sync_words(d["c"]["num_blocks_m"]), dtype=torch.int32, device="cuda")
     print(f"[fused full-size] {name}: tile then fused", flush=True)
     _check_against_tile(d, sync)
+    rows = d["prow"].long()
+    for t in ("hid", "out"):   # every valid row written (the sentinel is a NaN) and finite
+        assert bool(torch.isfinite(d[t][rows]).all()), f"{t}: valid rows unwritten or non-finite"
     first = d["out"].clone()
     _fused(d, sync)
     assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
