@@ -58,7 +58,8 @@ typedef enum rmoe_status {
     RMOE_ERR_MISALIGNED = -3,        /* a tensor pointer not 16-byte aligned */
     RMOE_ERR_LAUNCH = -4,            /* the HIP runtime refused a launch */
     RMOE_ERR_CONTRACT = -5,          /* tables violate the dispatch contract */
-    RMOE_ERR_CAPACITY = -6           /* an output table is too small */
+    RMOE_ERR_CAPACITY = -6,          /* an output table is too small */
+    RMOE_ERR_SCRATCH = -7            /* a batch beyond the library's static scratch */
 } rmoe_status;
 
 /* Kernel family for the forward (RMOE_VARIANT_AUTO picks by shape). */
@@ -339,6 +340,33 @@ RMOE_API int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tok
                                         int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair,
                                         int32_t *bad_ids, void *workspace, size_t workspace_bytes,
                                         void *stream);
+
+/*
+ * rmoe_build_contract_device without the workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same tables, same
+ * arguments otherwise, same asynchronous launches on `stream`; the scratch
+ * (contract_chunks * (E + 1) per-chunk counts, as rmoe_contract_workspace_
+ * bytes counts them) lives in a static device array of the library,
+ * rmoe_contract_noalloc_max_words() int32 words (1 MiB) per GPU, held by each
+ * GPU the library runs on until the process ends; nothing in it needs to
+ * start at zero, and the call never allocates or frees.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and corrupt each
+ * other's tables; serialise them.  A batch whose scratch exceeds the array
+ * (e.g. E = 128 with more than about 4.1 M pairs) returns RMOE_ERR_SCRATCH
+ * before anything is launched; other errors as rmoe_build_contract_device.
+ */
+RMOE_API size_t rmoe_contract_noalloc_max_words(void);
+RMOE_API int rmoe_build_contract_device_noalloc(const int32_t *topk_ids, int64_t num_tokens,
+                                                int32_t top_k, int32_t num_experts,
+                                                int32_t *group_sizes, int32_t *group_offsets,
+                                                int32_t *group_padded_offsets,
+                                                int32_t *group_idx_for_bx,
+                                                int64_t capacity_blocks, int32_t *num_blocks_m,
+                                                int32_t *order, int32_t *padded_row_of_pair,
+                                                int32_t *compact_pos_of_pair, int32_t *bad_ids,
+                                                void *stream);
 
 /*
  * Router (write-up "MetaX-TileLang工具链", section 2.4: the reference router

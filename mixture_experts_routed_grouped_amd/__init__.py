@@ -58,6 +58,9 @@ _SIGS = {
     "rmoe_router_f16": ([_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "rmoe_build_contract_device": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                     _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "rmoe_contract_noalloc_max_words": ([], ctypes.c_size_t),
+    "rmoe_build_contract_device_noalloc": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _P, _P,
+                                            _P, _P, _P], ctypes.c_int),
 }
 
 
@@ -450,6 +453,33 @@ def build_contract_device(topk_ids, num_experts: int, stream=None, out=None) -> 
     _check(st, "rmoe_build_contract_device")
     out["_workspace"] = ws  # keeps the scratch alive until the stream has used it
     out.update(num_blocks_m=nb.value, total_padded_tokens=Tp, pairs=pairs)
+    return out
+
+
+def build_contract_device_noalloc(topk_ids, num_experts: int, out: dict, stream=None) -> dict:
+    """rmoe_build_contract_device_noalloc: the same tables as
+    ``build_contract_device``, written into the caller's ``out`` tensors
+    (a dict as that function returns, for the same T, k and E), with the
+    library's static scratch instead of a workspace: nothing is allocated.
+    Calls that overlap in time on one GPU share that scratch and race."""
+    torch = _torch()
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
+    T, k = topk_ids.shape
+    pairs, E = T * k, int(num_experts)
+    if out.get("pairs") != pairs or out["group_sizes"].numel() != E:
+        raise ValueError("out was built for another shape")
+    nb = ctypes.c_int32(0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib().rmoe_build_contract_device_noalloc(
+        _dev(topk_ids, torch.int32, "topk_ids") if pairs else ctypes.c_void_p(0),
+        T, k, E, ptr(out["group_sizes"]), ptr(out["group_offsets"]),
+        ptr(out["group_padded_offsets"]), ptr(out["group_idx_for_bx"]),
+        out["group_idx_for_bx"].numel(), ctypes.byref(nb), ptr(out["order"]),
+        ptr(out["padded_row_of_pair"]), ptr(out["compact_pos_of_pair"]), ptr(out["bad_ids"]),
+        _stream(topk_ids, stream))
+    _check(st, "rmoe_build_contract_device_noalloc")
+    out["num_blocks_m"] = nb.value
     return out
 
 

@@ -129,6 +129,7 @@ const char *rmoe_status_str(int status) {
         case RMOE_ERR_LAUNCH: return "kernel launch failed";
         case RMOE_ERR_CONTRACT: return "tables violate the dispatch contract";
         case RMOE_ERR_CAPACITY: return "output table too small";
+        case RMOE_ERR_SCRATCH: return "batch exceeds the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -408,6 +409,42 @@ size_t rmoe_contract_workspace_bytes(int64_t num_pairs, int32_t num_experts) {
     return n > 0 ? n * sizeof(int32_t) : 4;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the device contract build (both entry points), before
+// any HIP call; on success *M holds the block count.  The scratch is
+// checked by the caller.
+int check_contract_device(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                          int32_t num_experts, const int32_t *group_sizes,
+                          const int32_t *group_offsets, const int32_t *group_padded_offsets,
+                          const int32_t *group_idx_for_bx, int64_t capacity_blocks,
+                          const int32_t *num_blocks_m, const int32_t *order,
+                          const int32_t *padded_row_of_pair, const int32_t *compact_pos_of_pair,
+                          const int32_t *bad_ids, int64_t *M) {
+    if (num_tokens < 0 || top_k < 0 || num_experts < 1 || !num_blocks_m) return RMOE_ERR_INVALID_ARGUMENT;
+    if (num_experts > kMaxDeviceExperts) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    const int64_t pairs = num_tokens * top_k;
+    if (pairs > INT32_MAX / 2) return RMOE_ERR_INVALID_ARGUMENT;
+    *M = ceil_div(pairs, B) + num_experts;
+    if (*M * B > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
+    if (!group_sizes || !group_offsets || !group_padded_offsets || !group_idx_for_bx || !bad_ids)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (pairs > 0 && (!topk_ids || !order || !padded_row_of_pair || !compact_pos_of_pair))
+        return RMOE_ERR_INVALID_ARGUMENT;
+    if (capacity_blocks < *M) return RMOE_ERR_CAPACITY;
+    if (!aligned4(topk_ids) || !aligned4(group_sizes) || !aligned4(group_offsets) ||
+        !aligned4(group_padded_offsets) || !aligned4(group_idx_for_bx) || !aligned4(order) ||
+        !aligned4(padded_row_of_pair) || !aligned4(compact_pos_of_pair) || !aligned4(bad_ids))
+        return RMOE_ERR_MISALIGNED;
+    return RMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
                                int32_t num_experts, int32_t *group_sizes, int32_t *group_offsets,
                                int32_t *group_padded_offsets, int32_t *group_idx_for_bx,
@@ -415,30 +452,50 @@ int rmoe_build_contract_device(const int32_t *topk_ids, int64_t num_tokens, int3
                                int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair,
                                int32_t *bad_ids, void *workspace, size_t workspace_bytes,
                                void *stream) {
-    if (num_tokens < 0 || top_k < 0 || num_experts < 1 || !num_blocks_m) return RMOE_ERR_INVALID_ARGUMENT;
-    if (num_experts > kMaxDeviceExperts) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    int64_t M = 0;
+    int st = check_contract_device(topk_ids, num_tokens, top_k, num_experts, group_sizes,
+                                   group_offsets, group_padded_offsets, group_idx_for_bx,
+                                   capacity_blocks, num_blocks_m, order, padded_row_of_pair,
+                                   compact_pos_of_pair, bad_ids, &M);
+    if (st != RMOE_OK) return st;
     const int64_t pairs = num_tokens * top_k;
-    if (pairs > INT32_MAX / 2) return RMOE_ERR_INVALID_ARGUMENT;
-    const int64_t M = ceil_div(pairs, B) + num_experts;
-    if (M * B > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
-    if (!group_sizes || !group_offsets || !group_padded_offsets || !group_idx_for_bx || !bad_ids ||
-        !workspace)
-        return RMOE_ERR_INVALID_ARGUMENT;
-    if (pairs > 0 && (!topk_ids || !order || !padded_row_of_pair || !compact_pos_of_pair))
-        return RMOE_ERR_INVALID_ARGUMENT;
-    if (capacity_blocks < M) return RMOE_ERR_CAPACITY;
+    if (!workspace) return RMOE_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < rmoe_contract_workspace_bytes(pairs, num_experts)) return RMOE_ERR_CAPACITY;
-    if (!aligned4(topk_ids) || !aligned4(group_sizes) || !aligned4(group_offsets) ||
-        !aligned4(group_padded_offsets) || !aligned4(group_idx_for_bx) || !aligned4(order) ||
-        !aligned4(padded_row_of_pair) || !aligned4(compact_pos_of_pair) || !aligned4(bad_ids) ||
-        !aligned4(workspace))
-        return RMOE_ERR_MISALIGNED;
+    if (!aligned4(workspace)) return RMOE_ERR_MISALIGNED;
     *num_blocks_m = (int32_t)M;
     return to_status(rmoe::launch_contract(topk_ids, pairs, num_experts, (int32_t)M, group_sizes,
                                            group_offsets, group_padded_offsets, group_idx_for_bx,
                                            order, padded_row_of_pair, compact_pos_of_pair, bad_ids,
                                            static_cast<int32_t *>(workspace),
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t rmoe_contract_noalloc_max_words(void) { return (size_t)rmoe::kNoAllocScratchWords; }
+
+int rmoe_build_contract_device_noalloc(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
+                                       int32_t num_experts, int32_t *group_sizes,
+                                       int32_t *group_offsets, int32_t *group_padded_offsets,
+                                       int32_t *group_idx_for_bx, int64_t capacity_blocks,
+                                       int32_t *num_blocks_m, int32_t *order,
+                                       int32_t *padded_row_of_pair, int32_t *compact_pos_of_pair,
+                                       int32_t *bad_ids, void *stream) {
+    int64_t M = 0;
+    int st = check_contract_device(topk_ids, num_tokens, top_k, num_experts, group_sizes,
+                                   group_offsets, group_padded_offsets, group_idx_for_bx,
+                                   capacity_blocks, num_blocks_m, order, padded_row_of_pair,
+                                   compact_pos_of_pair, bad_ids, &M);
+    if (st != RMOE_OK) return st;
+    const int64_t pairs = num_tokens * top_k;
+    // the scratch this batch needs, against the static array (nothing is allocated)
+    const size_t cap = (size_t)rmoe::kNoAllocScratchWords * sizeof(int32_t);
+    if (rmoe_contract_workspace_bytes(pairs, num_experts) > cap) return RMOE_ERR_SCRATCH;
+    int32_t *ws = nullptr;  // this device's copy of the static scratch
+    if (rmoe::noalloc_scratch(&ws) != hipSuccess) return RMOE_ERR_LAUNCH;
+    *num_blocks_m = (int32_t)M;
+    return to_status(rmoe::launch_contract(topk_ids, pairs, num_experts, (int32_t)M, group_sizes,
+                                           group_offsets, group_padded_offsets, group_idx_for_bx,
+                                           order, padded_row_of_pair, compact_pos_of_pair, bad_ids,
+                                           ws, static_cast<hipStream_t>(stream)));
 }
 
 // ---- router ----------------------------------------------------------------

@@ -19,10 +19,38 @@
 // get -1 as padded row and compact position, and are counted in *bad.
 // A batch that fits one chunk (decode-sized) runs all four steps in one
 // workgroup and one launch, with the same arithmetic.
+#include <atomic>
+
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
 namespace rmoe {
+
+// Library-owned scratch of the contract build that allocates nothing
+// (rmoe_build_contract_device_noalloc): the per-chunk expert counts, kept in
+// one static array per GPU for the life of the process.  Host code never
+// passes `scratch` itself (on the host that name is only a stand-in): its
+// device address is fetched once per device with hipGetSymbolAddress.
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchWords];
+
+hipError_t noalloc_scratch(int32_t **ptr) {
+    static std::atomic<int32_t *> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int32_t *p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<int32_t *>(addr);
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int TPB = 256;

@@ -71,6 +71,13 @@ hipError_t launch_validate(const int32_t *gs, const int32_t *go, const int32_t *
                            const int32_t *gidx, int32_t E, int32_t M, int64_t pairs,
                            int32_t *violations, hipStream_t s);
 
+// Words of the static scratch the allocation-free contract build uses
+// (1 MiB per GPU): contract_chunks(pairs) * (E + 1) must not exceed it.
+constexpr int64_t kNoAllocScratchWords = (int64_t)1 << 18;
+// Device address of that scratch on the current device (looked up once per
+// device, cached).
+hipError_t noalloc_scratch(int32_t **ptr);
+
 // Device-side contract build.  ws holds contract_chunks(pairs) * (E + 1)
 // int32 of scratch.
 int64_t contract_chunks(int64_t pairs);

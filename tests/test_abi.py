@@ -264,3 +264,25 @@ def test_binding_holds_no_contract_arithmetic():
     for name in ("bench.py", "__graft_entry__.py"):
         text = open(os.path.join(ROOT, name)).read()
         assert "32 * E" not in text and "-(-" not in text, name
+
+
+def test_noalloc_contract_limits_without_gpu():
+    """The allocation-free contract build checks its batch against the static
+    scratch before any HIP call."""
+    L = R.lib()
+    fake = ctypes.c_void_p(0x10000)
+    nb = ctypes.c_int32(-1)
+    words = L.rmoe_contract_noalloc_max_words()
+    assert words == 1 << 18
+
+    def na(T, k, E, cap=10 ** 7):
+        return L.rmoe_build_contract_device_noalloc(fake, T, k, E, fake, fake, fake, fake, cap,
+                                                    ctypes.byref(nb), fake, fake, fake, fake, None)
+
+    # E = 8192: 49 chunks of 2048 pairs need 49 * 8193 words > 2^18
+    assert na(100000, 1, 8192) == -7
+    assert na(-1, 1, 4) == -1
+    assert na(10, 1, 8193) == -2
+    assert na(300, 1, 4, cap=4) == -6
+    assert nb.value == -1
+    assert R.status_str(-7).startswith("batch exceeds")
