@@ -10,7 +10,8 @@ three self-checks ``check_coverage``, ``check_padded_covers_compact`` and
 signature and the Step-1/Step-2 row predicate in "Fused MoE GEMM 提交说明",
 section 完整算子代码, plus the section 实现要点 (padded vs compact indexing).
 
-Plain Python lists and loops on purpose: this is the definition, not a fast
+Plain Python lists, loops and standard-library primitives (a bucket sort,
+prefix sums, a bisection) on purpose: this is the definition, not a fast
 implementation.
 
 Readings of points the pages leave open:
@@ -24,6 +25,10 @@ Readings of points the pages leave open:
 """
 from __future__ import annotations
 
+import bisect
+import collections
+import itertools
+
 BLOCK = 128  # block_token == padding_M in both pages
 
 
@@ -34,14 +39,17 @@ def ceil_div(a: int, b: int) -> int:
 def build_contract(topk_ids, n_experts: int, block: int = BLOCK) -> dict:
     """Group tables for a routing ``topk_ids`` (T rows of k expert ids).
 
-    Steps as in the tutorial's ``build_contract``:
-      1. flatten (token, slot) pairs in token-major then slot order;
-      2. stable sort of the pairs by expert -> ``order``; per-expert counts;
-         exclusive prefix sum -> ``group_offsets`` (compact starts);
-      3. padded starts: each expert occupies ceil((count + 1) / block) * block
-         rows (the "+1" leaves one slack row per expert);
-      4. ``m_blocks = ceil(pairs / block) + E`` and, per block bx, the last
-         expert whose padded start is <= bx * block.
+    What the tutorial's ``build_contract`` defines, step by step:
+      1. the routed pairs are the (token, slot) entries in token-major then
+         slot order, pair p = t*k + j;
+      2. the pairs sorted by expert, ties in ascending p -> ``order``; the
+         expert group sizes; their exclusive prefix sums -> ``group_offsets``
+         (where each expert's rows start in compact order);
+      3. each expert occupies ceil((count + 1) / block) * block padded rows
+         (the "+1" leaves one slack row), their prefix sums ->
+         ``group_padded_offsets``;
+      4. ``m_blocks = ceil(pairs / block) + E`` blocks, block bx belonging to
+         the last expert whose padded start is <= bx * block.
     Packing (where each pair lands) follows section 实现要点 of the
     submission notes: tokens use padded row indices, routed weights use
     compact indices ``group_offsets[e] + token_offset``.
@@ -49,50 +57,38 @@ def build_contract(topk_ids, n_experts: int, block: int = BLOCK) -> dict:
     E = int(n_experts)
     if E < 1:
         raise ValueError("need at least one expert")
-    # 1) flatten
-    flat_expert: list[int] = []
-    flat_token: list[int] = []
-    for t, row in enumerate(topk_ids):
-        for e in row:
-            e = int(e)
-            if not 0 <= e < E:
-                raise ValueError(f"expert id {e} out of range [0, {E})")
-            flat_expert.append(e)
-            flat_token.append(t)
-    pairs = len(flat_expert)
+    # 1) the routed pairs, p = t*k + j
+    pair_list = [(t, int(e)) for t, row in enumerate(topk_ids) for e in row]
+    for _, e in pair_list:
+        if not 0 <= e < E:
+            raise ValueError(f"expert id {e} out of range [0, {E})")
+    flat_token = [t for t, _ in pair_list]
+    flat_expert = [e for _, e in pair_list]
+    pairs = len(pair_list)
 
-    # 2) stable sort by expert, counts, compact offsets (E+1 entries)
-    order = sorted(range(pairs), key=lambda p: flat_expert[p])
-    counts = [0] * E
-    for e in flat_expert:
-        counts[e] += 1
-    group_offsets = [0] * (E + 1)
-    for e in range(E):
-        group_offsets[e + 1] = group_offsets[e] + counts[e]
+    # 2) counting sort: one bucket per expert, filled in ascending p (stable)
+    buckets: list[list[int]] = [[] for _ in range(E)]
+    for p, e in enumerate(flat_expert):
+        buckets[e].append(p)
+    order = [p for bucket in buckets for p in bucket]
+    counts = [len(bucket) for bucket in buckets]
+    group_offsets = list(itertools.accumulate(counts, initial=0))        # E+1 entries
 
-    # 3) padded offsets (E+1 entries)
-    group_padded_offsets = [0] * (E + 1)
-    for e in range(E):
-        span = ceil_div(counts[e] + 1, block) * block
-        group_padded_offsets[e + 1] = group_padded_offsets[e] + span
+    # 3) padded spans and their prefix sums (E+1 entries)
+    spans = [ceil_div(c + 1, block) * block for c in counts]
+    group_padded_offsets = list(itertools.accumulate(spans, initial=0))
 
-    # 4) block count and block -> expert table (linear scan as on the page)
+    # 4) blocks: the padded starts are strictly increasing, so "the last
+    #    expert whose start is <= bx*block" is a right bisection
     m_blocks = ceil_div(pairs, block) + E
-    group_idx_for_bx = []
-    for bx in range(m_blocks):
-        start = bx * block
-        g = 0
-        for i in range(E):
-            if start >= group_padded_offsets[i]:
-                g = i
-        group_idx_for_bx.append(g)
+    starts = group_padded_offsets[:E]
+    group_idx_for_bx = [bisect.bisect_right(starts, bx * block) - 1 for bx in range(m_blocks)]
 
     # packing maps: the r-th pair of expert e (in sorted order)
     padded_row_of_pair = [0] * pairs
     compact_pos_of_pair = [0] * pairs
-    for e in range(E):
-        for r in range(counts[e]):
-            p = order[group_offsets[e] + r]
+    for e, bucket in enumerate(buckets):
+        for r, p in enumerate(bucket):
             padded_row_of_pair[p] = group_padded_offsets[e] + r
             compact_pos_of_pair[p] = group_offsets[e] + r
 
@@ -137,10 +133,11 @@ def valid_rows(c: dict):
 def check_coverage(c: dict) -> None:
     """Every (token, expert) pair appears exactly once (tutorial check 1),
     and ``order`` is a permutation of the pairs."""
-    seen = list(zip(c["flat_token"], c["flat_expert"]))
-    assert len(seen) == len(set(seen)), "a (token, expert) pair appears twice"
-    assert sum(c["group_sizes"]) == c["pairs"] == len(seen)
-    assert sorted(c["order"]) == list(range(c["pairs"])), "order is not a permutation"
+    tally = collections.Counter((c["flat_token"][p], c["flat_expert"][p]) for p in c["order"])
+    assert all(n == 1 for n in tally.values()), "a (token, expert) pair appears twice"
+    assert sum(tally.values()) == sum(c["group_sizes"]) == c["pairs"]
+    assert collections.Counter(c["order"]) == collections.Counter(range(c["pairs"])), \
+        "order is not a permutation"
 
 
 def check_padded_covers_compact(c: dict) -> None:
