@@ -115,7 +115,8 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
     contract build from device top-k ids, the pack, the combine, and the
     whole layer -- router, device contract, pack, both expert kernels,
     combine -- with no host round trip; for the tiled family also the
-    single-launch forward beside the two-launch one."""
+    single-launch forward, in both hand-overs (hidden rows kept in one XCD's
+    L2, or handed across XCDs through memory), beside the two-launch one."""
     import torch
     import mixture_experts_routed_grouped_amd as R
     import workloads
@@ -158,8 +159,10 @@ def aux_timings(cfg, inp, hid, out, variant, reps=20):
         tables = (d["group_sizes"], d["group_offsets"], d["group_padded_offsets"], d["group_idx_for_bx"])
         steps["forward_two_launch"] = lambda: R.forward(stacked, inp.wg, inp.wu, inp.wd, w_compact,
                                                         *tables, hid, out, variant="tile")
-        steps["forward_fused"] = lambda: R.forward_fused(stacked, inp.wg, inp.wu, inp.wd, w_compact,
-                                                         *tables, hid, out, sync=sync)
+        for ho in ("local", "global"):
+            steps[f"forward_fused_{ho}"] = (
+                lambda ho=ho: R.forward_fused(stacked, inp.wg, inp.wu, inp.wd, w_compact, *tables,
+                                              hid, out, sync=sync, handover=ho))
     res = {}
     for name, fn in steps.items():
         for _ in range(3):

@@ -210,12 +210,20 @@ RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const v
  * hidden intermediate's global write and re-read, and kernel fusion as the
  * way to cut it).  Same arguments, layouts and results as
  * rmoe_forward_f16_variant with RMOE_VARIANT_TILE, on any shape; meant for
- * prefill-shaped batches.  One persistent kernel runs every gate/up tile,
- * then every down tile; a down tile starts as soon as all gate/up tiles of
- * its own pair of blocks have published their hidden rows, so the two
- * stages overlap at the hand-over (the workspace is still written: it is
- * the hand-over buffer, not a second output).  Results are bit-identical to
- * the two-launch tiled forward.
+ * prefill-shaped batches.  One persistent kernel runs every gate/up tile and
+ * every down tile; a down tile starts as soon as all gate/up tiles of its own
+ * pair of blocks have published their hidden rows, so the two stages overlap
+ * (the workspace is still written: it is the hand-over buffer, not a second
+ * output).  Results are bit-identical to the two-launch tiled forward.
+ *   handover: RMOE_FUSED_LOCAL runs each pair of blocks' gate/up and down
+ *         tiles on one XCD (the one whose queue a workgroup reads from the
+ *         XCC_ID register), so its hidden rows are handed over inside that
+ *         XCD's L2 and leave it only when evicted; RMOE_FUSED_GLOBAL spreads
+ *         a pair's tiles over all XCDs and hands the rows over through memory
+ *         (write-through stores, device-scope acquire); RMOE_FUSED_AUTO takes
+ *         GLOBAL, measured the faster on every workload: the L2 is write-back,
+ *         so LOCAL still writes every hidden row out on eviction, and running
+ *         each pair's slices on one XCD raises operand reads beyond L2.
  *   sync: int32 device scratch of rmoe_fused_sync_words(num_blocks_m) words,
  *         caller-owned.  It must be all zero before its first use; every
  *         call that runs to completion leaves it zero again, except
@@ -228,14 +236,17 @@ RMOE_API int rmoe_forward_f16_variant(const void *stacked_expert_tokens, const v
  *   max_wait_us: how long a down tile may wait for its pair's hidden rows;
  *         <= 0 selects the default, 2 s (real waits last at most one
  *         gate/up stage, i.e. milliseconds).
- * Returns as rmoe_forward_f16; the launch is asynchronous, nothing is read
- * back.
+ * Returns as rmoe_forward_f16 (RMOE_ERR_INVALID_ARGUMENT for an unknown
+ * handover); the launch is asynchronous, nothing is read back.
  */
 #define RMOE_FUSED_SYNC_TICKETS 0 /* [8] one work queue per locality group */
 #define RMOE_FUSED_SYNC_EXIT 8    /* workgroups done */
 #define RMOE_FUSED_SYNC_ERROR 9   /* sticky: skipped tiles */
 #define RMOE_FUSED_SYNC_ABORT 10  /* this launch gave up waiting (reset on exit) */
 #define RMOE_FUSED_SYNC_HEAD 16   /* then [num_blocks_m]: gate/up tiles done per pair */
+#define RMOE_FUSED_AUTO 0
+#define RMOE_FUSED_LOCAL 1
+#define RMOE_FUSED_GLOBAL 2
 RMOE_API size_t rmoe_fused_sync_words(int32_t num_blocks_m);
 RMOE_API int rmoe_forward_fused_f16(const void *stacked_expert_tokens, const void *gate_w,
                                     const void *up_w, const void *down_w,
@@ -246,7 +257,7 @@ RMOE_API int rmoe_forward_fused_f16(const void *stacked_expert_tokens, const voi
                                     int32_t *sync, int64_t hidden, int64_t intermediate,
                                     int32_t num_experts, int64_t total_padded_tokens,
                                     int64_t total_valid_tokens, int32_t num_blocks_m,
-                                    int32_t max_wait_us, void *stream);
+                                    int32_t max_wait_us, int32_t handover, void *stream);
 
 /*
  * Stage 1 alone (the Step-1 grid of section 完整算子代码): workspace rows =

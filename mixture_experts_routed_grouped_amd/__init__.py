@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "librmoe.so")
 VARIANT_AUTO, VARIANT_STREAM, VARIANT_TILE = 0, 1, 2
 _VARIANTS = {"auto": 0, "stream": 1, "tile": 2, 0: 0, 1: 1, 2: 2}
 _VARIANT_NAMES = {VARIANT_STREAM: "stream", VARIANT_TILE: "tile"}
+_HANDOVER = {"auto": 0, "local": 1, "global": 2}
 
 
 class RmoeError(RuntimeError):
@@ -49,7 +50,8 @@ _SIGS = {
     "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
                                  ctypes.c_int),
     "rmoe_fused_sync_words": ([_I32], ctypes.c_size_t),
-    "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
+    "rmoe_forward_fused_f16": ([_P] * 12 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _I32, _P],
+                               ctypes.c_int),
     "rmoe_gate_up_f16": ([_P] * 7 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_down_f16": ([_P] * 8 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P], ctypes.c_int),
     "rmoe_pack_f16": ([_P] * 4 + [_I64, _I32, _I64, _P, _P, _I64, _P], ctypes.c_int),
@@ -285,14 +287,16 @@ def fused_sync_errors(sync, clear: bool = True) -> int:
 
 def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_weights, group_sizes,
                   group_offsets, group_padded_offsets, group_idx_for_bx, workspace, out, sync=None,
-                  max_wait_us=0, stream=None):
+                  max_wait_us=0, handover="auto", stream=None):
     """Both stages in one launch (rmoe_forward_fused_f16): same arguments and
     results as forward(..., variant="tile"); ``sync`` is the int32 queue
     state (default: a zeroed buffer cached per device, size and stream;
     calls sharing one must not overlap in time); ``max_wait_us`` bounds a
     down tile's wait for its hidden rows (0: the library's default).  A wait
     that times out skips its tile and counts it in the sync buffer's error
-    word: check it with ``fused_sync_errors(sync)`` before using ``out``."""
+    word: check it with ``fused_sync_errors(sync)`` before using ``out``.
+    ``handover``: "local" (each pair's hidden rows stay in one XCD's L2),
+    "global" (handed over through memory) or "auto" (the library's choice)."""
     torch = _torch()
     x = stacked_expert_tokens
     E, I, H = gate_w.shape
@@ -319,7 +323,8 @@ def forward_fused(stacked_expert_tokens, gate_w, up_w, down_w, routed_expert_wei
         _dev(group_padded_offsets, i32, "group_padded_offsets"),
         _dev(group_idx_for_bx, i32, "group_idx_for_bx"), _dev(workspace, f16, "workspace"),
         _dev(out, f16, "out"), _dev(sync, i32, "sync"), H, I, E, Tp,
-        routed_expert_weights.numel(), M, int(max_wait_us), _stream(x, stream))
+        routed_expert_weights.numel(), M, int(max_wait_us), _HANDOVER[handover],
+        _stream(x, stream))
     _check(st, "rmoe_forward_fused_f16")
 
 

@@ -61,6 +61,14 @@ int stream_tiles(int64_t pairs, int32_t num_experts) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? RMOE_OK : RMOE_ERR_LAUNCH; }
 
+// Hand-over of the single launch.  AUTO hands hidden rows across XCDs: the
+// XCD-local hand-over is correct on every shape but measured slower on all
+// workloads (large 14.0 against 10.9 ms, fine 1.28-1.36 against 0.92 ms):
+// a write-back L2 still writes every hidden row out, and running each
+// entry's slices on one XCD raises the operand traffic beyond L2 by ~20%.
+int pick_handover(int32_t handover) {
+    return handover == RMOE_FUSED_LOCAL ? RMOE_FUSED_LOCAL : RMOE_FUSED_GLOBAL;
+}
 int gate_up_impl(const void *x, const void *gate_w, const void *up_w, const int32_t *gs,
                  const int32_t *gpo, const int32_t *gidx, void *workspace, int64_t hidden,
                  int64_t intermediate, int32_t E, int64_t Tp, int32_t M, int64_t pairs,
@@ -330,10 +338,11 @@ int rmoe_forward_fused_f16(const void *x, const void *gate_w, const void *up_w,
                            void *workspace, void *out, int32_t *sync, int64_t hidden,
                            int64_t intermediate, int32_t num_experts, int64_t total_padded_tokens,
                            int64_t total_valid_tokens, int32_t num_blocks_m, int32_t max_wait_us,
-                           void *stream) {
+                           int32_t handover, void *stream) {
     int st = check_dims(hidden, intermediate, num_experts, total_padded_tokens, num_blocks_m);
     if (st != RMOE_OK) return st;
-    if (total_valid_tokens < 0) return RMOE_ERR_INVALID_ARGUMENT;
+    if (total_valid_tokens < 0 || handover < RMOE_FUSED_AUTO || handover > RMOE_FUSED_GLOBAL)
+        return RMOE_ERR_INVALID_ARGUMENT;
     if (!x || !gate_w || !up_w || !down_w || !gs || !go || !gpo || !workspace || !out || !sync ||
         (num_blocks_m > 0 && !gidx) || (total_valid_tokens > 0 && !rw))
         return RMOE_ERR_INVALID_ARGUMENT;
@@ -365,7 +374,9 @@ int rmoe_forward_fused_f16(const void *x, const void *gate_w, const void *up_w,
         a->pairs = total_valid_tokens;
     }
     const int64_t wait_us = max_wait_us > 0 ? max_wait_us : kFusedWaitUs;
-    return to_status(rmoe::launch_fused(gu, dn, sync, wait_us, static_cast<hipStream_t>(stream)));
+    const bool local = pick_handover(handover) == RMOE_FUSED_LOCAL;
+    return to_status(
+        rmoe::launch_fused(gu, dn, sync, wait_us, local, static_cast<hipStream_t>(stream)));
 }
 
 int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,

@@ -51,9 +51,12 @@ hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s);
 hipError_t launch_tile_down(const StageArgs &a, hipStream_t s);
 // Both tiled stages in one persistent launch (gu.y = dn.x = the hidden
 // workspace); sync as described for rmoe_forward_fused_f16; a down tile
-// waits at most wait_us for its pair's hidden rows.
+// waits at most wait_us for its pair's hidden rows.  local: each XCD runs
+// whole entries and the hidden rows stay in its L2 (the kernel's LOCAL
+// mode); otherwise entries are spread over all XCDs with write-through
+// hand-over.
 hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int64_t wait_us,
-                        hipStream_t s);
+                        bool local, hipStream_t s);
 
 hipError_t launch_pack(const _Float16 *x, const float *topk_w, const int32_t *prow,
                        const int32_t *cpos, int64_t pairs, int32_t top_k, int64_t H, int64_t Tp,

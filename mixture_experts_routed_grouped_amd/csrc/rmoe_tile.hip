@@ -366,37 +366,69 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
 // ---- Both stages in one launch.
 //
 // The same tiles as the two persistent launches, taken from one queue per
-// locality group (workgroup w serves group w % 8, i.e. its XCD): first the
-// group's gate/up items, then its down items, in the orders above.  A down
-// item of the pair at block bx needs every gate/up slice of that pair in the
-// hidden workspace, so gate/up items count themselves into done[bx] once
-// their stores are out, and a down item waits until done[bx] reaches the
-// slice count.  The XCDs' L2 caches are not coherent with each other: the
-// gate/up tiles of this launch store their hidden rows with device-scope
-// (sc1) write-through stores and wait for them to complete before counting
-// -- the effect of an agent-scope release without writing back the whole L2,
-// which measured ~2-5% of the launch -- and a down tile drops its CU's and
-// XCD's stale copies (agent-scope acquire) before reading them.
-// Progress: a workgroup waits only while holding a down ticket, i.e. after
-// every gate/up ticket of its own queue was handed to a running workgroup,
-// and gate/up items never wait; so every wait ends once one workgroup of each
-// queue runs.  Each wait is bounded all the same, by wait_ticks of the
-// constant-rate real-time counter: a wait that gives up skips its item, adds
-// 1 to the sticky error word and raises the launch's abort flag, after which
-// every wait gives up at once, so the kernel always exits within about one
+// locality group.  A down item of the pair at block bx needs every gate/up
+// slice of that pair in the hidden workspace, so gate/up items count
+// themselves into done[bx] once their stores are out, and a down item waits
+// until done[bx] reaches the slice count.  Two ways to keep the hand-over
+// coherent, the XCDs' L2 caches not being coherent with each other:
+//
+// LOCAL (hidden kept in one XCD's L2): a workgroup serves the queue of the
+//   XCD it runs on (read from the XCC_ID hardware register, so the
+//   placement is known, not assumed); each entry's gate/up and down slices
+//   all belong to that one queue (fused_seq / fused_ticket in rmoe_sched.h),
+//   so producer and consumer of a hidden row share the XCD's L2: gate/up
+//   stores are ordinary write-back stores, counted once they have completed
+//   into L2, and a down tile only drops its CU's L1 (buffer_inv sc0) after
+//   its wait.  Hidden rows then move beyond L2 only when the L2 evicts them.
+//   Progress: every gate/up ticket of an entry precedes its down tickets in
+//   the same queue, so a waiting workgroup waits only for tickets already
+//   handed to running workgroups of its own XCD, whatever else is resident.
+//   A queue that no workgroup served (an XCD with no workgroup of this
+//   launch) is drained by the last workgroup out, which then runs those
+//   entries' gate/up slices before their down slices itself.
+// global (hidden handed across XCDs; used when a pair's hidden rows would
+//   not fit an L2 or there are too few entries to balance 8 queues):
+//   workgroup w serves group w % 8; a group's queue holds its gate/up items,
+//   then its down items, in the orders of the two persistent launches.  The
+//   gate/up tiles store their hidden rows with device-scope (sc1)
+//   write-through stores and wait for them to complete before counting --
+//   the effect of an agent-scope release without writing back the whole L2,
+//   which measured ~2-5% of the launch -- and a down tile drops its CU's and
+//   XCD's stale copies (agent-scope acquire) before reading them.  Progress:
+//   a workgroup waits only while holding a down ticket, i.e. after every
+//   gate/up ticket of its own queue was handed to a running workgroup, and
+//   gate/up items never wait; so every wait ends once one workgroup of each
+//   queue runs (dispatch in workgroup order gives every queue one of the
+//   first eight workgroups).
+// Each wait is bounded all the same, by wait_ticks of the constant-rate
+// real-time counter: a wait that gives up skips its item, adds 1 to the
+// sticky error word and raises the launch's abort flag, after which every
+// wait gives up at once, so the kernel always exits within about one
 // deadline.  The last workgroup out returns the tickets, the counters, the
 // abort flag and the exit count to zero, ready for the next launch.
-__global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, int32_t *sync,
-                                                    uint64_t wait_ticks) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__device__ __forceinline__ int xcc_id() {
+    return (int)__builtin_amdgcn_s_getreg((3 << 11) | 20);  // hwreg(HW_REG_XCC_ID, 0, 4)
+}
+
+template <bool LOCAL>
+__device__ void serve_queue(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
+                            uint64_t wait_ticks, int grp, unsigned char *smem) {
     int *bcast = reinterpret_cast<int *>(smem);  // LDS is idle between items
     int32_t *tickets = sync + RMOE_FUSED_SYNC_TICKETS;
     int32_t *done = sync + RMOE_FUSED_SYNC_HEAD;
     const int NT1 = (int)(gu.N / 128), NT2 = (int)((dn.N + 255) / 256);
-    const int grp = blockIdx.x % kXcd;
-    const TileSeq seq1 = tile_seq(gu.gs, gu.E, NT1, grp, kXcd), seq2 = tile_seq(dn.gs, dn.E, NT2, grp, kXcd);
-    const int n1 = seq1.n, n2 = seq2.n;
-    TileCursor cur;
+    FusedSeq fq{};
+    TileSeq seq1{}, seq2{};
+    int n_all;
+    if constexpr (LOCAL) {
+        fq = fused_seq(gu.gs, gu.E, NT1, NT2, grp, kXcd);
+        n_all = fq.n;
+    } else {
+        seq1 = tile_seq(gu.gs, gu.E, NT1, grp, kXcd);
+        seq2 = tile_seq(dn.gs, dn.E, NT2, grp, kXcd);
+        n_all = seq1.n + seq2.n;
+    }
+    TileCursor cur, cur_dn;
     for (;;) {
         __syncthreads();  // every wave is done with the LDS of the last item
         if (threadIdx.x == 0)
@@ -404,20 +436,32 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
                                               __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         const int t = bcast[0];
-        if (t >= n1 + n2) break;
-        if (t < n1) {
-            const TileItem it = tile_item(gu.gs, gu.gpo, seq1, t, cur);
+        if (t >= n_all) break;
+        bool down;
+        TileItem it;
+        if constexpr (LOCAL) {
+            const FusedTicket k = fused_ticket(fq, t);
+            if (k.j >= fq.J) continue;  // void ticket of the padded last unit
+            down = k.down;
+            if (down)
+                it = entry_item(gu.gs, gu.gpo, fq.lo + k.j, k.nt, cur_dn);
+            else
+                it = entry_item(gu.gs, gu.gpo, fq.lo + k.j, k.nt, cur);
+        } else {
+            down = t >= seq1.n;
+            it = down ? tile_item(dn.gs, dn.gpo, seq2, t - seq1.n, cur)
+                      : tile_item(gu.gs, gu.gpo, seq1, t, cur);
+        }
+        if (!down) {
             __syncthreads();  // the ticket is read before the DMAs reuse its LDS word
-            run_item<true, true>(gu, smem, it);
-            // the hidden rows went out write-through at device scope; once
-            // every wave's stores have completed they are visible to all
-            // XCDs, and the count may go up (no L2 write-back needed)
-            wait_vm<0>();
+            // LOCAL: write-back stores into this XCD's L2; global: write-through
+            // at device scope, visible to every XCD once completed
+            run_item<true, !LOCAL>(gu, smem, it);
+            wait_vm<0>();  // this wave's hidden stores have completed
             __syncthreads();
             if (threadIdx.x == 0)
                 __hip_atomic_fetch_add(done + it.bx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            const TileItem it = tile_item(dn.gs, dn.gpo, seq2, t - n1, cur);
             if (threadIdx.x == 0) {
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                 bool ready;
@@ -431,8 +475,14 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
                         break;
                     __builtin_amdgcn_s_sleep(8);
                 }
-                // acquire: drop this CU's and XCD's stale copies before any wave reads
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                // acquire before any wave reads (the barrier below orders
+                // their loads after it): LOCAL drops this CU's L1 only (the
+                // rows sit in this XCD's L2); global also drops the XCD's
+                // stale L2 copies
+                if constexpr (LOCAL)
+                    asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+                else
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 if (!ready) {
                     __hip_atomic_fetch_add(sync + RMOE_FUSED_SYNC_ERROR, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
@@ -448,19 +498,44 @@ __global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, 
             run_item<false>(dn, smem, it);
         }
     }
-    // the last workgroup out resets the queue state (the error word stays)
-    __syncthreads();  // every wave has read the final ticket
-    if (threadIdx.x == 0)
-        bcast[0] = __hip_atomic_fetch_add(sync + RMOE_FUSED_SYNC_EXIT, 1, __ATOMIC_ACQ_REL,
-                                          __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (bcast[0]) {
-        for (int i = threadIdx.x; i < kXcd; i += blockDim.x) tickets[i] = 0;
-        for (int i = threadIdx.x; i < gu.M; i += blockDim.x) done[i] = 0;
-        if (threadIdx.x == 0) {
-            sync[RMOE_FUSED_SYNC_ABORT] = 0;
-            sync[RMOE_FUSED_SYNC_EXIT] = 0;
+}
+
+template <bool LOCAL>
+__global__ __launch_bounds__(256) void fused_kernel(StageArgs gu, StageArgs dn, int32_t *sync,
+                                                    uint64_t wait_ticks) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int *bcast = reinterpret_cast<int *>(smem);
+    int32_t *tickets = sync + RMOE_FUSED_SYNC_TICKETS;
+    int32_t *done = sync + RMOE_FUSED_SYNC_HEAD;
+    // first the queue of this workgroup's group; then, in the last workgroup
+    // out only (every other one has finished), LOCAL runs every queue no
+    // workgroup served (none ran on that XCD) -- a served queue is already
+    // drained, its ticket past its end.  One call site keeps one inlined copy.
+    int g = LOCAL ? __builtin_amdgcn_readfirstlane(xcc_id()) % kXcd : (int)(blockIdx.x % kXcd);
+    bool last = false;
+    for (;;) {
+        serve_queue<LOCAL>(gu, dn, sync, wait_ticks, g, smem);
+        if (!last) {
+            __syncthreads();  // every wave has read the final ticket
+            if (threadIdx.x == 0)
+                bcast[0] = __hip_atomic_fetch_add(sync + RMOE_FUSED_SYNC_EXIT, 1, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+            __syncthreads();
+            if (!bcast[0]) return;
+            last = true;
+            if (!LOCAL) break;
+            g = 0;
+        } else if (++g == kXcd) {
+            break;
         }
+    }
+    // reset the queue state (the error word stays)
+    __syncthreads();
+    for (int i = threadIdx.x; i < kXcd; i += blockDim.x) tickets[i] = 0;
+    for (int i = threadIdx.x; i < gu.M; i += blockDim.x) done[i] = 0;
+    if (threadIdx.x == 0) {
+        sync[RMOE_FUSED_SYNC_ABORT] = 0;
+        sync[RMOE_FUSED_SYNC_EXIT] = 0;
     }
 }
 
@@ -525,7 +600,7 @@ hipError_t launch_tile_down(const StageArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync, int64_t wait_us,
-                        hipStream_t s) {
+                        bool local, hipStream_t s) {
     unsigned grid = 0;
     hipError_t e = persistent_grid(grid);
     if (e != hipSuccess) return e;
@@ -533,11 +608,18 @@ hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
     e = wall_clock_khz(khz);
     if (e != hipSuccess) return e;
     const unsigned lds = LDS_BYTES;
-    static std::atomic<uint64_t> lds_set{0};
-    e = lds_opt_in_once((const void *)fused_kernel, (int)lds, lds_set);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fused_kernel, dim3(grid), dim3(256), lds, s, gu, dn, sync,
-                       (uint64_t)khz * (uint64_t)wait_us / 1000u);
+    const uint64_t ticks = (uint64_t)khz * (uint64_t)wait_us / 1000u;
+    if (local) {
+        static std::atomic<uint64_t> lds_set{0};
+        e = lds_opt_in_once((const void *)fused_kernel<true>, (int)lds, lds_set);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fused_kernel<true>, dim3(grid), dim3(256), lds, s, gu, dn, sync, ticks);
+    } else {
+        static std::atomic<uint64_t> lds_set{0};
+        e = lds_opt_in_once((const void *)fused_kernel<false>, (int)lds, lds_set);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fused_kernel<false>, dim3(grid), dim3(256), lds, s, gu, dn, sync, ticks);
+    }
     return hipGetLastError();
 }
 

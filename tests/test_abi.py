@@ -190,8 +190,8 @@ def test_fused_argument_errors_without_gpu():
     fake = ctypes.c_void_p(0x10000)
     odd = ctypes.c_void_p(0x10002)
 
-    def fz(H=256, I=128, E=4, Tp=640, pairs=18, M=5, sync=fake, x=fake):
-        return L.rmoe_forward_fused_f16(x, *([fake] * 10), sync, H, I, E, Tp, pairs, M, 0, None)
+    def fz(H=256, I=128, E=4, Tp=640, pairs=18, M=5, sync=fake, x=fake, ho=0):
+        return L.rmoe_forward_fused_f16(x, *([fake] * 10), sync, H, I, E, Tp, pairs, M, 0, ho, None)
 
     assert L.rmoe_fused_sync_words(5) == 16 + 5
     assert L.rmoe_fused_sync_words(-1) == 0
@@ -202,6 +202,8 @@ def test_fused_argument_errors_without_gpu():
     assert fz(x=odd) == -3
     assert fz(sync=ctypes.c_void_p(0x10002)) == -3        # int32 words
     assert fz(M=0, Tp=0, pairs=0) == 0                    # no blocks: nothing launched
+    assert fz(ho=3) == -1                                 # unknown hand-over
+    assert fz(ho=-1) == -1
 
 
 def test_contract_sizes_and_variant_queries():

@@ -18,10 +18,10 @@ from _oracle_run import run as oracle_run
 pytestmark = pytest.mark.gpu
 
 
-def _fused(d, sync=None):
+def _fused(d, sync=None, handover="auto"):
     fresh_outputs(d)
     R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"], d["go"],
-                    d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync)
+                    d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, handover=handover)
     torch.cuda.synchronize()
     return d
 
@@ -32,12 +32,12 @@ def _sync_clean(sync):
     assert not s.any(), f"queue state not reset: {np.nonzero(s)[0][:8]}"
 
 
-def _check_against_tile(d, sync):
+def _check_against_tile(d, sync, handover="auto"):
     """Fused vs the two-launch tiled path on the same inputs, bit for bit."""
     forward(d, "tile")
     rows = d["prow"].long()
     want_out, want_hid = d["out"][rows].clone(), d["hid"][rows].clone()
-    _fused(d, sync)
+    _fused(d, sync, handover)
     mask = valid_row_mask(d)
     assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
     assert torch.equal(d["out"][rows].view(torch.int16), want_out.view(torch.int16)), "out differs"
@@ -45,11 +45,12 @@ def _check_against_tile(d, sync):
     _sync_clean(sync)
 
 
-def _small(inp):
+def _small(inp, handover="auto"):
     d = prepare(inp)
     sync = torch.zeros(R.fused_sync_words(d["c"]["num_blocks_m"]), dtype=torch.int32, device="cuda")
-    print(f"[fused] {inp.cfg.name}: pairs={d['c']['pairs']} E={d['E']} H={d['H']} I={d['I']}", flush=True)
-    _check_against_tile(d, sync)
+    print(f"[fused] {inp.cfg.name} ({handover}): pairs={d['c']['pairs']} E={d['E']} H={d['H']} "
+          f"I={d['I']}", flush=True)
+    _check_against_tile(d, sync, handover)
     if d["c"]["pairs"] == 0:
         return
     orc = oracle_run(inp)
@@ -61,8 +62,12 @@ def _small(inp):
     assert (err <= 2e-2 + 2e-2 * np.abs(want)).all(), float(err.max())
 
 
-def test_fused_tiny():
-    _small(workloads.make_inputs(workloads.CONFIGS["tiny"]))
+HANDOVERS = ["local", "global"]
+
+
+@pytest.mark.parametrize("handover", HANDOVERS)
+def test_fused_tiny(handover):
+    _small(workloads.make_inputs(workloads.CONFIGS["tiny"]), handover)
 
 
 @pytest.mark.parametrize("seed,E,k,T,H,I,routing", [
@@ -73,21 +78,24 @@ def test_fused_tiny():
     (5, 40, 4, 3000, 512, 1024, "zipf"),     # more tiles than workgroups in both stages
     (6, 12, 2, 2000, 256, 2304, "uniform"),  # 18 gate/up slices per pair
 ])
-def test_fused_random_shapes(seed, E, k, T, H, I, routing):
+@pytest.mark.parametrize("handover", HANDOVERS)
+def test_fused_random_shapes(seed, E, k, T, H, I, routing, handover):
     cfg = workloads.Config(f"f{seed}", T, E, k, H, I, routing=routing, zipf_s=1.4, seed=seed)
-    _small(workloads.make_inputs(cfg))
+    _small(workloads.make_inputs(cfg), handover)
 
 
-def test_fused_edge_groups_and_empty():
+@pytest.mark.parametrize("handover", HANDOVERS)
+def test_fused_edge_groups_and_empty(handover):
     counts = [0, 127, 128, 129, 256, 0, 1, 3]
     ids = workloads.routing_from_counts(counts, seed=5)
     cfg = workloads.Config("fedge", ids.shape[0], len(counts), 1, 256, 256, seed=5)
-    _small(workloads.make_inputs(cfg, topk_ids=ids))
+    _small(workloads.make_inputs(cfg, topk_ids=ids), handover)
     cfg = workloads.Config("fempty", 0, 4, 2, 128, 128, seed=6)
-    _small(workloads.make_inputs(cfg, topk_ids=np.zeros((0, 2), np.int32)))
+    _small(workloads.make_inputs(cfg, topk_ids=np.zeros((0, 2), np.int32)), handover)
 
 
-def test_fused_shared_sync_two_calls():
+@pytest.mark.parametrize("handover", HANDOVERS)
+def test_fused_shared_sync_two_calls(handover):
     """One sync buffer for two calls in a row, the second on a smaller batch:
     both correct, the buffer clean after each."""
     big = prepare(workloads.make_inputs(workloads.Config("fs1", 3000, 40, 4, 512, 1024,
@@ -95,32 +103,37 @@ def test_fused_shared_sync_two_calls():
     small = prepare(workloads.make_inputs(workloads.Config("fs2", 300, 5, 2, 256, 384,
                                                            routing="zipf", zipf_s=1.4, seed=1)))
     sync = torch.zeros(R.fused_sync_words(big["c"]["num_blocks_m"]), dtype=torch.int32, device="cuda")
-    print("[fused] shared sync: large then small batch", flush=True)
-    _check_against_tile(big, sync)
-    _check_against_tile(small, sync)
+    print(f"[fused] shared sync ({handover}): large then small batch", flush=True)
+    _check_against_tile(big, sync, handover)
+    _check_against_tile(small, sync, handover)
 
 
-@pytest.mark.parametrize("name", ["prefill", "fine", "large"])
-def test_fused_full_size(name):
+@pytest.mark.parametrize("name,handover", [("prefill", "global"), ("fine", "local"),
+                                           ("large", "local"), ("fine", "global"),
+                                           ("prefill", "local")])
+def test_fused_full_size(name, handover):
     """Full-size workloads: bit-equal to the two-launch tiled path (whose rows
-    the full-size parity test samples against the oracle), padding rows
-    untouched, and a second call bit-identical on the same sync buffer."""
+    the full-size parity test checks against the oracle), padding rows
+    untouched, every valid row written, and a second call bit-identical on
+    the same sync buffer -- in both hand-overs (hidden rows handed across
+    XCDs through memory, the library's choice; or kept inside one XCD)."""
     cfg = workloads.CONFIGS[name]
-    print(f"[fused full-size] {name}: inputs", flush=True)
+    print(f"[fused full-size] {name} ({handover}): inputs", flush=True)
     d = prepare(workloads.make_inputs(cfg, device="cuda"))
     sync = torch.zeros(R.fused_sync_words(d["c"]["num_blocks_m"]), dtype=torch.int32, device="cuda")
     print(f"[fused full-size] {name}: tile then fused", flush=True)
-    _check_against_tile(d, sync)
+    _check_against_tile(d, sync, handover)
     rows = d["prow"].long()
     for t in ("hid", "out"):   # every valid row written (the sentinel is a NaN) and finite
         assert bool(torch.isfinite(d[t][rows]).all()), f"{t}: valid rows unwritten or non-finite"
     first = d["out"].clone()
-    _fused(d, sync)
+    _fused(d, sync, handover)
     assert torch.equal(first.view(torch.int16), d["out"].view(torch.int16)), "not deterministic"
     _sync_clean(sync)
 
 
-def test_fused_wait_timeout_from_host():
+@pytest.mark.parametrize("handover", HANDOVERS)
+def test_fused_wait_timeout_from_host(handover):
     """Failure handling, forced from the host: a 1 µs bound on the down
     tiles' wait makes them give up while gate/up tiles are still running.
     The launch still ends, counts the skipped tiles in the error word, writes
@@ -134,10 +147,11 @@ def test_fused_wait_timeout_from_host():
     forward(d, "tile")
     rows = d["prow"].long()
     want_out, want_hid = d["out"][rows].clone(), d["hid"][rows].clone()
-    print("[fused] forced wait timeout (1 us)", flush=True)
+    print(f"[fused] forced wait timeout (1 us, {handover})", flush=True)
     fresh_outputs(d)
     R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"], d["go"],
-                    d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, max_wait_us=1)
+                    d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, max_wait_us=1,
+                    handover=handover)
     torch.cuda.synchronize()
     s = sync.cpu().numpy()
     skipped = int(s[R.FUSED_SYNC_ERROR])
@@ -151,6 +165,6 @@ def test_fused_wait_timeout_from_host():
     assert bool(ok.all()), "an aborted launch wrote wrong output values"
     assert bool((got == SENTINEL).any()), "skipped tiles should leave their rows unwritten"
     sync.zero_()
-    _fused(d, sync)
+    _fused(d, sync, handover)
     assert torch.equal(d["out"][rows].view(torch.int16), want_out.view(torch.int16))
     _sync_clean(sync)
