@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only sweep the streaming/tiled forward times across batch sizes under "
+                         "Zipf routing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), the "
                          "reference that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
@@ -269,8 +272,9 @@ def measure(cfg, variant, steps, warmup, with_aux=False):
     R.pack(inp.x, topk_w, prow, cpos, stacked, w_compact)
     hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
     out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
-    # the family the library runs for this batch (its own choice, asked through the C-ABI)
-    resolved = R.pick_variant(c["pairs"], E, variant)
+    # the family for this batch: the library's choice, asked through the C-ABI
+    # with the largest group from the host tables
+    resolved = R.pick_variant(c["pairs"], E, variant, max_group_rows=int(max(c["group_sizes"])))
 
     def step(evs=None):
         if evs is not None:
@@ -342,10 +346,73 @@ def measure(cfg, variant, steps, warmup, with_aux=False):
     return res, inp, c
 
 
+# token counts of the crossover sweep, per (E, top_k, H, I, Zipf s): skewed
+# routing at decode-to-mid batch sizes, the shapes of the workloads
+CROSSOVER = {
+    "E128_k8_H7168_I2048_zipf1.2": (128, 8, 7168, 2048, 1.2, [16, 32, 64, 128, 256, 512]),
+    "E64_k6_H2048_I1408_zipf1.1": (64, 6, 2048, 1408, 1.1, [32, 64, 128, 192, 256, 384, 512]),
+    "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 256]),
+}
+
+
+def crossover_sweep(reps=20):
+    """Forward time of both kernel families across batch sizes under Zipf
+    routing (one JSON line per batch), with the family the library picks
+    from the average alone and from the average and the largest group."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_grouped_amd as R
+    import workloads
+    dev = torch.device("cuda:0")
+    for name, (E, k, H, I, zs, Ts) in CROSSOVER.items():
+        base = workloads.make_inputs(workloads.Config("sweep", max(Ts), E, k, H, I, routing="zipf",
+                                                      zipf_s=zs), device=dev)
+        for T in Ts:
+            ids = workloads.draw_routing(workloads.Config("sweep", T, E, k, H, I, routing="zipf",
+                                                          zipf_s=zs))
+            c = R.build_contract(ids, E)
+            i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+            tabs = [i32(c[q]) for q in ("group_sizes", "group_offsets", "group_padded_offsets",
+                                        "group_idx_for_bx")]
+            Tp = c["total_padded_tokens"]
+            stacked = torch.zeros((Tp, H), dtype=torch.float16, device=dev)
+            wc = torch.zeros(c["pairs"], dtype=torch.float32, device=dev)
+            tw = torch.from_numpy(workloads.draw_routed_weights(T, k, 7).reshape(-1).copy()).to(dev)
+            R.pack(base.x[:T].contiguous(), tw, i32(c["padded_row_of_pair"]),
+                   i32(c["compact_pos_of_pair"]), stacked, wc)
+            hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
+            out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
+            res = {}
+            for v in ("stream", "tile"):
+                fn = lambda: R.forward(stacked, base.wg, base.wu, base.wd, wc, *tabs, hid, out, variant=v)
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                res[v + "_us"] = round(e0.elapsed_time(e1) / reps * 1e3, 1)
+            gmax = int(max(c["group_sizes"]))
+            print(json.dumps({"sweep": name, "tokens": T, "pairs": c["pairs"],
+                              "avg_rows": round(c["pairs"] / E, 1), "max_rows": gmax,
+                              "auto_avg": R.pick_variant(c["pairs"], E),
+                              "auto_max": R.pick_variant(c["pairs"], E, max_group_rows=gmax),
+                              **res}), flush=True)
+        del base
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib, args.steps)
+        return
+    if args.crossover:
+        crossover_sweep()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

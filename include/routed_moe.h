@@ -158,16 +158,25 @@ RMOE_API int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t
                                  int64_t *total_padded_tokens);
 
 /*
- * The kernel family the forward, rmoe_gate_up_f16 and rmoe_down_f16 run for
- * a batch: `variant` itself if it is RMOE_VARIANT_STREAM or _TILE, else
- * (RMOE_VARIANT_AUTO) the choice from num_pairs and num_experts alone --
- * the same function every entry point calls, so the two stages of one batch
- * always agree.  AUTO streams while the batch averages at most 32 routed
- * rows per expert (there an expert's GEMM is bound by reading its weights,
- * as the contract tutorial's closing note says of small M) and tiles above.
- * Returns RMOE_VARIANT_STREAM or RMOE_VARIANT_TILE, or a negative status.
+ * The kernel family for a batch: `variant` itself if it is
+ * RMOE_VARIANT_STREAM or _TILE; for RMOE_VARIANT_AUTO, streaming while the
+ * batch averages at most 32 routed rows per expert (there an expert's GEMM
+ * is bound by reading its weights, as the contract tutorial's closing note
+ * says of small M) and, when max_group_rows >= 0 (the largest group size,
+ * known to a caller that holds host tables), while every expert fits one
+ * 128-row block -- under skewed routing the largest experts' blocks would
+ * otherwise take several streaming passes, each reading their weights
+ * again -- and tiling otherwise.  max_group_rows < 0 means unknown: the
+ * forward, rmoe_gate_up_f16 and rmoe_down_f16 never read device tables,
+ * so their AUTO is this function with max_group_rows = -1 (the two stages
+ * of one batch therefore always agree); pass the family this returns as
+ * their `variant` to use the largest group.
+ * Returns RMOE_VARIANT_STREAM or RMOE_VARIANT_TILE, or
+ * RMOE_ERR_INVALID_ARGUMENT (unknown variant, negative pairs, E < 1,
+ * max_group_rows > num_pairs).
  */
-RMOE_API int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts);
+RMOE_API int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts,
+                               int64_t max_group_rows);
 
 /*
  * The fused expert FFN forward (the submission's run_kernel, with the

@@ -45,7 +45,7 @@ _SIGS = {
     "rmoe_validate_contract_device": ([_P, _P, _P, _P, _I32, _I32, _I64, _I64, _P, _P], ctypes.c_int),
     "rmoe_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "rmoe_contract_sizes": ([_I64, _I32, _P, _P], ctypes.c_int),
-    "rmoe_pick_variant": ([_I32, _I64, _I32], ctypes.c_int),
+    "rmoe_pick_variant": ([_I32, _I64, _I32, _I64], ctypes.c_int),
     "rmoe_forward_f16": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _P], ctypes.c_int),
     "rmoe_forward_f16_variant": ([_P] * 11 + [_I64, _I64, _I32, _I64, _I64, _I32, _I32, _P],
                                  ctypes.c_int),
@@ -178,10 +178,13 @@ def contract_sizes(num_pairs: int, num_experts: int) -> tuple[int, int]:
     return int(m.value), int(tp.value)
 
 
-def pick_variant(num_pairs: int, num_experts: int, variant="auto") -> str:
-    """The kernel family ("stream" or "tile") the library runs for a batch
-    (rmoe_pick_variant: the choice every forward and stage entry makes)."""
-    v = int(lib().rmoe_pick_variant(_VARIANTS[variant], int(num_pairs), int(num_experts)))
+def pick_variant(num_pairs: int, num_experts: int, variant="auto", max_group_rows: int = -1) -> str:
+    """The kernel family ("stream" or "tile") for a batch (rmoe_pick_variant).
+    With the default max_group_rows=-1 it is the choice every forward and
+    stage entry makes under AUTO; with the largest group size (host tables)
+    it also weighs the skew."""
+    v = int(lib().rmoe_pick_variant(_VARIANTS[variant], int(num_pairs), int(num_experts),
+                                    int(max_group_rows)))
     _check(min(v, 0), "rmoe_pick_variant")
     return _VARIANT_NAMES[v]
 

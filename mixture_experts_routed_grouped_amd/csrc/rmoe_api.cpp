@@ -48,12 +48,20 @@ int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
 // (uniform routing): about 48 rows per expert for E=8 (H=4096, I=14336),
 // 40 for E=64 (2048, 1408), 28 for E=128 (7168, 2048); at 32 streaming
 // wins or ties within 2% on all three.
+// Under skewed (Zipf) routing the crossover moves lower -- about 12-16 rows
+// per expert for E=128, 18-24 for E=64 -- because the largest experts'
+// blocks need several streaming passes, each reading their weights again.
+// So when the caller knows the largest group (max_group_rows >= 0, from
+// host tables), streaming is kept only while every expert fits one block
+// (<= 128 rows, at most two 64-token passes).
 constexpr int64_t kStreamMaxRowsPerExpert = RMOE_STREAM_MAX_ROWS;
+constexpr int64_t kStreamMaxGroupRows = B;
 constexpr int64_t kStreamOneTile = 24;
-int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts) {
+int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts, int64_t max_group_rows = -1) {
     if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
-    return pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts ? RMOE_VARIANT_STREAM
-                                                                   : RMOE_VARIANT_TILE;
+    const bool few = pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts;
+    const bool fits = max_group_rows < 0 || max_group_rows <= kStreamMaxGroupRows;
+    return few && fits ? RMOE_VARIANT_STREAM : RMOE_VARIANT_TILE;
 }
 int stream_tiles(int64_t pairs, int32_t num_experts) {
     return pairs <= kStreamOneTile * (int64_t)num_experts ? 1 : 2;
@@ -229,9 +237,11 @@ int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t *num_blo
     return RMOE_OK;
 }
 
-int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts) {
-    if (bad_variant(variant) || num_pairs < 0 || num_experts < 1) return RMOE_ERR_INVALID_ARGUMENT;
-    return pick_variant(variant, num_pairs, num_experts);
+int rmoe_pick_variant(int32_t variant, int64_t num_pairs, int32_t num_experts,
+                      int64_t max_group_rows) {
+    if (bad_variant(variant) || num_pairs < 0 || num_experts < 1 || max_group_rows > num_pairs)
+        return RMOE_ERR_INVALID_ARGUMENT;
+    return pick_variant(variant, num_pairs, num_experts, max_group_rows);
 }
 
 int rmoe_validate_contract_device(const int32_t *gs, const int32_t *go, const int32_t *gpo,

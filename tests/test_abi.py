@@ -227,9 +227,16 @@ def test_contract_sizes_and_variant_queries():
     assert R.pick_variant(8192, 8) == "tile"                # prefill workload
     assert R.pick_variant(8192, 8, "stream") == "stream"
     assert R.pick_variant(128, 8, "tile") == "tile"
-    assert L.rmoe_pick_variant(7, 10, 4) == -1
-    assert L.rmoe_pick_variant(0, -1, 4) == -1
-    assert L.rmoe_pick_variant(0, 10, 0) == -1
+    assert L.rmoe_pick_variant(7, 10, 4, -1) == -1
+    assert L.rmoe_pick_variant(0, -1, 4, -1) == -1
+    assert L.rmoe_pick_variant(0, 10, 0, -1) == -1
+    assert L.rmoe_pick_variant(0, 10, 4, 11) == -1        # a group larger than the batch
+    # the largest group weighs in when known: every expert must fit one block
+    assert R.pick_variant(2048, 128, max_group_rows=120) == "stream"
+    assert R.pick_variant(2048, 128, max_group_rows=242) == "tile"   # Zipf 1.2, 256 tokens
+    assert R.pick_variant(128, 8, max_group_rows=23) == "stream"     # decode workload
+    assert R.pick_variant(4096, 8, max_group_rows=100) == "tile"     # the average decides first
+    assert R.pick_variant(2048, 128, "stream", max_group_rows=242) == "stream"
 
 
 def test_validate_device_argument_errors_without_gpu():
