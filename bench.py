@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep the streaming/tiled forward times across batch sizes under "
                          "Zipf routing")
+    ap.add_argument("--dense-compare", action="store_true",
+                    help="only time the tiled stages on one expert (a dense SwiGLU FFN) beside "
+                         "torch's fp16 matmul on the same GEMM shapes")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), the "
                          "reference that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
@@ -406,6 +409,64 @@ def crossover_sweep(reps=20):
         torch.cuda.empty_cache()
 
 
+def dense_compare(reps=20):
+    """The tiled stages on the dense special case of the method -- one expert,
+    8192 tokens, H=4096, I=14336 (a plain SwiGLU FFN; gate/up is then an
+    8192 x 28672 x 4096 GEMM, down 8192 x 4096 x 14336) -- beside torch's
+    fp16 matmul (the vendor BLAS) on the same shapes, same box, same run: how
+    far the tiled kernels are from the best dense GEMM the chip runs."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_grouped_amd as R
+    import workloads
+    dev = torch.device("cuda:0")
+    T, H, I = 8192, 4096, 14336
+    cfg = workloads.Config("dense", T, 1, 1, H, I)
+    inp = workloads.make_inputs(cfg, device=dev, topk_ids=np.zeros((T, 1), np.int32))
+    c = R.build_contract(inp.topk_ids, 1)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    gs, go, gpo, gidx = (i32(c[q]) for q in ("group_sizes", "group_offsets", "group_padded_offsets",
+                                             "group_idx_for_bx"))
+    Tp = c["total_padded_tokens"]
+    stacked = torch.zeros((Tp, H), dtype=torch.float16, device=dev)
+    wc = torch.zeros(T, dtype=torch.float32, device=dev)
+    R.pack(inp.x, torch.ones(T, dtype=torch.float32, device=dev), i32(c["padded_row_of_pair"]),
+           i32(c["compact_pos_of_pair"]), stacked, wc)
+    hid = torch.empty((Tp, I), dtype=torch.float16, device=dev)
+    out = torch.empty((Tp, H), dtype=torch.float16, device=dev)
+
+    def tm(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    gu = tm(lambda: R.gate_up(stacked, inp.wg, inp.wu, gs, gpo, gidx, hid, T, variant="tile"))
+    dn = tm(lambda: R.down(hid, inp.wd, wc, gs, go, gpo, gidx, out, variant="tile"))
+    x, wgu = inp.x.contiguous(), torch.cat([inp.wg[0], inp.wu[0]], 0).contiguous()  # [2I, H]
+    y1 = torch.empty((T, 2 * I), dtype=torch.float16, device=dev)
+    h = hid[:T].contiguous()
+    wd = inp.wd[0].contiguous()
+    y2 = torch.empty((T, H), dtype=torch.float16, device=dev)
+    mm1 = tm(lambda: torch.matmul(x, wgu.t(), out=y1))
+    mm2 = tm(lambda: torch.matmul(h, wd.t(), out=y2))
+    f1, f2 = 4.0 * T * H * I, 2.0 * T * H * I
+    print(json.dumps({"dense_compare": f"one expert, {T} tokens, H={H}, I={I}",
+                      "gate_up_us": round(gu, 1), "gate_up_tflops": round(f1 / gu / 1e6, 1),
+                      "down_us": round(dn, 1), "down_tflops": round(f2 / dn / 1e6, 1),
+                      "vendor_gemm_gate_up_us": round(mm1, 1),
+                      "vendor_gemm_gate_up_tflops": round(f1 / mm1 / 1e6, 1),
+                      "vendor_gemm_down_us": round(mm2, 1),
+                      "vendor_gemm_down_tflops": round(f2 / mm2 / 1e6, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy_mib:
@@ -413,6 +474,9 @@ def main():
         return
     if args.crossover:
         crossover_sweep()
+        return
+    if args.dense_compare:
+        dense_compare()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
