@@ -77,6 +77,7 @@ def test_fused_tiny(handover):
     (4, 2, 1, 520, 128, 640, "uniform"),
     (5, 40, 4, 3000, 512, 1024, "zipf"),     # more tiles than workgroups in both stages
     (6, 12, 2, 2000, 256, 2304, "uniform"),  # 18 gate/up slices per pair
+    (8, 512, 2, 1500, 256, 384, "zipf"),     # mostly empty experts: queues over few live entries
 ])
 @pytest.mark.parametrize("handover", HANDOVERS)
 def test_fused_random_shapes(seed, E, k, T, H, I, routing, handover):

@@ -88,6 +88,8 @@ def test_tiny(variant):
     (4, 2, 1, 520, 128, 640, "uniform"),   # four full blocks per expert, long I
     (5, 40, 4, 3000, 512, 1024, "zipf"),   # more tiles than workgroup slots: each loops
     (6, 12, 2, 2000, 256, 2304, "uniform"),  # 18 gate/up slices: groups of 8, 8, 2
+    (7, 256, 8, 64, 256, 256, "uniform"),  # many experts, about 2 rows each, some empty
+    (8, 512, 2, 1500, 256, 384, "zipf"),   # mostly empty experts, a few multi-block ones
 ])
 def test_random_shapes(variant, seed, E, k, T, H, I, routing):
     cfg = workloads.Config(f"r{seed}", T, E, k, H, I, routing=routing, zipf_s=1.4, seed=seed)
