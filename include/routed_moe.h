@@ -88,8 +88,10 @@ RMOE_API const char *rmoe_version(void);
  *   order [pairs] (the sorted pair ids); padded_row_of_pair [pairs]
  *   (the token row in the padded layout); compact_pos_of_pair [pairs]
  *   (the routed-weight index).  order/padded/compact may be NULL.
- * Errors: RMOE_ERR_INVALID_ARGUMENT for an id out of range or a bad size,
- * RMOE_ERR_CAPACITY when capacity_blocks < ceil(pairs/128) + E.
+ * Errors: RMOE_ERR_INVALID_ARGUMENT for an id out of range or a bad size
+ * (including 128 * num_blocks_m beyond INT32_MAX, which the int32 padded
+ * offsets cannot hold), RMOE_ERR_CAPACITY when capacity_blocks <
+ * ceil(pairs/128) + E.  Nothing is written on error.
  */
 RMOE_API int rmoe_build_contract(const int32_t *topk_ids, int64_t num_tokens, int32_t top_k,
                                  int32_t num_experts, int32_t *group_sizes,

@@ -163,6 +163,10 @@ int rmoe_build_contract(const int32_t *topk_ids, int64_t num_tokens, int32_t top
     const int64_t pairs = num_tokens * top_k;
     if (pairs > INT32_MAX / 2) return RMOE_ERR_INVALID_ARGUMENT;
     const int32_t E = num_experts;
+    // every padded row index (up to 128*M) must fit the int32 tables
+    const int64_t M = ceil_div(pairs, B) + E;
+    if (M * B > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
+    if (capacity_blocks < M || (M > 0 && !group_idx_for_bx)) return RMOE_ERR_CAPACITY;
     // counts (and id range check before anything is written)
     std::vector<int64_t> cnt(E, 0);
     for (int64_t p = 0; p < pairs; ++p) {
@@ -170,9 +174,6 @@ int rmoe_build_contract(const int32_t *topk_ids, int64_t num_tokens, int32_t top
         if (e < 0 || e >= E) return RMOE_ERR_INVALID_ARGUMENT;
         cnt[e]++;
     }
-    const int64_t M = ceil_div(pairs, B) + E;
-    if (M > INT32_MAX) return RMOE_ERR_INVALID_ARGUMENT;
-    if (capacity_blocks < M || (M > 0 && !group_idx_for_bx)) return RMOE_ERR_CAPACITY;
     // compact and padded offsets (E+1 entries each)
     group_offsets[0] = 0;
     group_padded_offsets[0] = 0;

@@ -104,6 +104,10 @@ def test_build_contract_errors():
     st = L.rmoe_build_contract(p(ids), 300, 1, 4, p(gs), p(go), p(gpo), p(gidx), 1, p(M), None,
                                None, None)
     assert st == -6                                       # capacity too small
+    # 2^24 experts: 128 * num_blocks_m no longer fits the int32 padded offsets
+    st = L.rmoe_build_contract(p(ids), 300, 1, 1 << 24, p(gs), p(go), p(gpo), p(gidx), 1 << 30,
+                               p(M), None, None, None)
+    assert st == -1
 
 
 def test_argument_errors_without_gpu():
