@@ -64,6 +64,16 @@ constexpr int kCpolSc1 = 16;  // cache-policy operand of the buffer builtins: sc
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 static_assert(kItemRows == kBlockM, "work items are contract blocks");
 
+// One 1 KB global -> LDS DMA addressed as a wave-uniform base plus a 32-bit
+// per-lane byte offset (the scalar-base form of global_load_lds_dwordx4):
+// a K step moves only the base, in scalar registers, so no 64-bit vector
+// address add precedes each DMA (measured 2-3% faster on every workload than
+// full per-lane addresses).  Counted by vmcnt like a load.
+__device__ __forceinline__ void dma16_sb(const void *base, unsigned off, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+
 // One tile: blocks bx (b0: its expert, offset in the group, valid rows) and
 // bx+1 (rows1 valid rows; has1: it belongs to the same expert) against the
 // weight slice nt.  Called with the workgroup's LDS; leaves no DMA in flight.
@@ -88,36 +98,40 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
     // ---- DMA sources.  Wave w fills rows 64 w .. 64 w + 63 of every slot,
     //      RPD rows per instruction j: lane i takes row 64 w + RPD j + i / 8,
     //      physical chunk i % 8, i.e. logical chunk (i % 8) ^ swz(row).
+    //      Addresses are a wave-uniform base (the wave's first weight row in
+    //      its matrix, the pair's first token row) plus per-lane byte offsets
+    //      (under 256 rows x K x 2 bytes with K <= 2^20: they fit 32 bits).
     const unsigned sbase = (unsigned)(uintptr_t)smem;
     const int64_t n0 = DUAL ? (int64_t)nt * 128 : (int64_t)nt * 256;  // first output feature
-    const _Float16 *wsrc[DMA_HALF], *tsrc[DMA_HALF];
+    const _Float16 *wmat = a.w0;
+    int64_t wrow0 = n0 + 64 * wave;
+    if constexpr (DUAL) {
+        wmat = wave < 2 ? a.w0 : a.w1;  // weight rows 0..127 gate, 128..255 up
+        wrow0 = n0 + ((64 * wave) & 127);
+    }
+    wrow0 = wrow0 < N ? wrow0 : N - 1;
+    const _Float16 *wbase = wmat + ((int64_t)b0.e * N + wrow0) * K;
+    const _Float16 *tbase = a.x + (int64_t)bx * kBlockM * K;
+    unsigned woff[DMA_HALF], tkoff[DMA_HALF];
 #pragma unroll
     for (int j = 0; j < DMA_HALF; ++j) {
         const int r = 64 * wave + RPD * j + lane / CPR;  // row within the slot
         const int c = (lane % CPR) ^ lds_swz(r);
-        int64_t row;
-        const _Float16 *mat;
-        if constexpr (DUAL) {
-            mat = r < 128 ? a.w0 : a.w1;  // weight rows 0..127 gate, 128..255 up
-            row = n0 + (r & 127);
-        } else {
-            mat = a.w0;
-            row = n0 + r;
-        }
+        int64_t row = DUAL ? n0 + (r & 127) : n0 + r;
         row = row < N ? row : N - 1;  // a narrow last slice: idle rows read a valid row
-        wsrc[j] = mat + ((int64_t)b0.e * N + row) * K + 8 * c;
-        int64_t trow = (int64_t)bx * kBlockM + r;  // token row r of the pair
-        if (r >= kBlockM && !has1) trow -= kBlockM;  // absent second block: stay in bounds
-        tsrc[j] = a.x + trow * K + 8 * c;
+        woff[j] = (unsigned)(((row - wrow0) * K + 8 * c) * 2);
+        int tr = r;                                 // token row r of the pair
+        if (r >= kBlockM && !has1) tr -= kBlockM;  // absent second block: stay in bounds
+        tkoff[j] = (unsigned)(((int64_t)tr * K + 8 * c) * 2);
     }
     const unsigned dwave = sbase + 64 * wave * ROWB;
     // DMA d of a step: d < DMA_HALF fills the token slot, the rest the weight slot
     auto dma_one = [&](int d, int kt_t, int kt_w, int slot_t, int slot_w) {
         if (d < DMA_HALF)
-            dma16(tsrc[d] + (int64_t)kt_t * BK, dwave + (NWS + slot_t) * SLOT + RPD * d * ROWB);
+            dma16_sb(tbase + (int64_t)kt_t * BK, tkoff[d], dwave + (NWS + slot_t) * SLOT + RPD * d * ROWB);
         else
-            dma16(wsrc[d - DMA_HALF] + (int64_t)kt_w * BK,
-                  dwave + slot_w * SLOT + RPD * (d - DMA_HALF) * ROWB);
+            dma16_sb(wbase + (int64_t)kt_w * BK, woff[d - DMA_HALF],
+                     dwave + slot_w * SLOT + RPD * (d - DMA_HALF) * ROWB);
     };
 
     // ---- MFMA operands of this wave: weight tiles t (32 rows each), token
