@@ -349,12 +349,17 @@ def measure(cfg, variant, steps, warmup, with_aux=False):
     return res, inp, c
 
 
-# token counts of the crossover sweep, per (E, top_k, H, I, Zipf s): skewed
-# routing at decode-to-mid batch sizes, the shapes of the workloads
+# token counts of the crossover sweep, per (E, top_k, H, I, Zipf s or None
+# for uniform routing): skewed routing at decode-to-mid batch sizes on the
+# shapes of the workloads, and uniform routing with few experts at 24-80
+# rows per expert
 CROSSOVER = {
     "E128_k8_H7168_I2048_zipf1.2": (128, 8, 7168, 2048, 1.2, [16, 32, 64, 128, 256, 512]),
     "E64_k6_H2048_I1408_zipf1.1": (64, 6, 2048, 1408, 1.1, [32, 64, 128, 192, 256, 384, 512]),
     "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 256]),
+    "E8_k2_H4096_I14336_uniform": (8, 2, 4096, 14336, None, [96, 128, 160, 192, 224, 256, 320]),
+    "E16_k2_H4096_I14336_uniform": (16, 2, 4096, 14336, None, [192, 256, 320, 384, 448, 512, 640]),
+    "E32_k4_H4096_I2048_uniform": (32, 4, 4096, 2048, None, [192, 256, 320, 384, 448, 512, 640]),
 }
 
 
@@ -369,11 +374,12 @@ def crossover_sweep(reps=20):
     import workloads
     dev = torch.device("cuda:0")
     for name, (E, k, H, I, zs, Ts) in CROSSOVER.items():
-        base = workloads.make_inputs(workloads.Config("sweep", max(Ts), E, k, H, I, routing="zipf",
-                                                      zipf_s=zs), device=dev)
+        routing = "zipf" if zs else "uniform"
+        base = workloads.make_inputs(workloads.Config("sweep", max(Ts), E, k, H, I, routing=routing,
+                                                      zipf_s=zs or 0.0), device=dev)
         for T in Ts:
-            ids = workloads.draw_routing(workloads.Config("sweep", T, E, k, H, I, routing="zipf",
-                                                          zipf_s=zs))
+            ids = workloads.draw_routing(workloads.Config("sweep", T, E, k, H, I, routing=routing,
+                                                          zipf_s=zs or 0.0))
             c = R.build_contract(ids, E)
             i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
             tabs = [i32(c[q]) for q in ("group_sizes", "group_offsets", "group_padded_offsets",

@@ -168,7 +168,11 @@ RMOE_API int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t
  * known to a caller that holds host tables), while every expert fits one
  * 128-row block -- under skewed routing the largest experts' blocks would
  * otherwise take several streaming passes, each reading their weights
- * again -- and tiling otherwise.  max_group_rows < 0 means unknown: the
+ * again -- and tiling otherwise.  With max_group_rows known it also
+ * streams batches of at most 32 experts whose every group fits one
+ * 64-token streaming pass (each weight byte is then read once, while the
+ * tiled family has too few work items to fill the GPU), whatever their
+ * average.  max_group_rows < 0 means unknown: the
  * forward, rmoe_gate_up_f16 and rmoe_down_f16 never read device tables,
  * so their AUTO is this function with max_group_rows = -1 (the two stages
  * of one batch therefore always agree); pass the family this returns as

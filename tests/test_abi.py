@@ -241,6 +241,13 @@ def test_contract_sizes_and_variant_queries():
     assert R.pick_variant(128, 8, max_group_rows=23) == "stream"     # decode workload
     assert R.pick_variant(4096, 8, max_group_rows=100) == "tile"     # the average decides first
     assert R.pick_variant(2048, 128, "stream", max_group_rows=242) == "stream"
+    # few experts, every group within one 64-token streaming pass: streaming
+    # even above 32 rows per expert on average
+    assert R.pick_variant(384, 8, max_group_rows=58) == "stream"     # E=8, 48 rows per expert
+    assert R.pick_variant(384, 8, max_group_rows=65) == "tile"       # a group needs two passes
+    assert R.pick_variant(384, 8) == "tile"                          # largest group unknown
+    assert R.pick_variant(1280, 32, max_group_rows=54) == "stream"   # E=32, 40 rows per expert
+    assert R.pick_variant(2560, 64, max_group_rows=54) == "tile"     # more than 32 experts
 
 
 def test_validate_device_argument_errors_without_gpu():
