@@ -356,8 +356,11 @@ def measure(cfg, variant, steps, warmup, with_aux=False):
 CROSSOVER = {
     "E128_k8_H7168_I2048_zipf1.2": (128, 8, 7168, 2048, 1.2, [16, 32, 64, 128, 256, 512]),
     "E64_k6_H2048_I1408_zipf1.1": (64, 6, 2048, 1408, 1.1, [32, 64, 128, 192, 256, 384, 512]),
-    "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 256]),
+    "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 224, 256]),
     "E8_k2_H4096_I14336_uniform": (8, 2, 4096, 14336, None, [96, 128, 160, 192, 224, 256, 320]),
+    "E8_k2_H6144_I16384_uniform": (8, 2, 6144, 16384, None, [128, 160, 192, 224, 256]),
+    "E8_k2_H2048_I5632_uniform": (8, 2, 2048, 5632, None, [128, 160, 192, 224, 256]),
+    "E4_k2_H4096_I14336_uniform": (4, 2, 4096, 14336, None, [64, 80, 96, 112, 128]),
     "E16_k2_H4096_I14336_uniform": (16, 2, 4096, 14336, None, [192, 256, 320, 384, 448, 512, 640]),
     "E32_k4_H4096_I2048_uniform": (32, 4, 4096, 2048, None, [192, 256, 320, 384, 448, 512, 640]),
 }

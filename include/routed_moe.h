@@ -164,7 +164,8 @@ RMOE_API int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t
  * RMOE_VARIANT_STREAM or _TILE; for RMOE_VARIANT_AUTO, streaming while the
  * batch averages at most 32 routed rows per expert (there an expert's GEMM
  * is bound by reading its weights, as the contract tutorial's closing note
- * says of small M) and, when max_group_rows >= 0 (the largest group size,
+ * says of small M), or at most 48 with at most 8 experts (the tiled family
+ * then has few work items), and, when max_group_rows >= 0 (the largest group size,
  * known to a caller that holds host tables), while every expert fits one
  * 128-row block -- under skewed routing the largest experts' blocks would
  * otherwise take several streaming passes, each reading their weights

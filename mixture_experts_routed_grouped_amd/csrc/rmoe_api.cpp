@@ -59,17 +59,26 @@ int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
 // once, while the tiled family has too few work items to fill the GPU
 // (E=8, H=4096: 128 down-stage items for 256 CUs).  Measured, uniform
 // routing: E=8 (4096, 14336) streams 18-22% faster at 40-48 rows per
-// expert, E=32 (4096, 2048) 3.6% at 40; E=16 stays within 2% either way;
+// expert, E=32 (4096, 2048) 4-16% at 40 (two boxes); E=16 within 4% either way;
 // for E=64 and E=128 tiling wins from about 30-40 rows, so the wider range
 // stops at 32 experts.
+// With at most 8 experts the average threshold is 48 rows: the tiled family
+// then has few work items (E=8, H=4096 gives its down stage 128 items for
+// 256 CUs).  Measured at 48 rows per expert, streaming takes less time on
+// every such batch: E=8 (4096, 14336) uniform 19% less and Zipf 1.2 2%,
+// E=8 (6144, 16384) 2.5%, E=8 (2048, 5632) 38%, E=4 (4096, 14336) 41%; at
+// 56 the two larger E=8 batches (Zipf, and 6144 x 16384) tile in 6-8% less.
 constexpr int64_t kStreamMaxRowsPerExpert = RMOE_STREAM_MAX_ROWS;
+constexpr int32_t kFewExperts = 8;
+constexpr int64_t kStreamMaxRowsFewExperts = 48;
 constexpr int64_t kStreamMaxGroupRows = B;
 constexpr int64_t kStreamOnePassRows = 64;
 constexpr int32_t kStreamOnePassMaxExperts = 32;
 constexpr int64_t kStreamOneTile = 24;
 int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts, int64_t max_group_rows = -1) {
     if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
-    const bool few = pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts;
+    const bool few = pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts ||
+                     (num_experts <= kFewExperts && pairs <= kStreamMaxRowsFewExperts * (int64_t)num_experts);
     const bool fits = max_group_rows < 0 || max_group_rows <= kStreamMaxGroupRows;
     const bool one_pass = max_group_rows >= 0 && max_group_rows <= kStreamOnePassRows &&
                           num_experts <= kStreamOnePassMaxExperts;

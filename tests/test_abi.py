@@ -224,10 +224,15 @@ def test_contract_sizes_and_variant_queries():
     assert L.rmoe_contract_sizes(10, 0, None, None) == -1
     assert L.rmoe_contract_sizes(2 ** 31, 4, None, None) == -1
     assert L.rmoe_contract_sizes(10, 4, None, None) == 0    # outputs are optional
-    # streaming while the batch averages at most 32 rows per expert, tiles above
+    # streaming while the batch averages at most 32 rows per expert (48 with
+    # at most 8 experts), tiles above
     assert R.pick_variant(128, 8) == "stream"               # decode workload
-    assert R.pick_variant(256, 8) == "stream"
-    assert R.pick_variant(257, 8) == "tile"
+    assert R.pick_variant(288, 9) == "stream"
+    assert R.pick_variant(289, 9) == "tile"
+    assert R.pick_variant(384, 8) == "stream"
+    assert R.pick_variant(385, 8) == "tile"
+    assert R.pick_variant(192, 4) == "stream"
+    assert R.pick_variant(193, 4) == "tile"
     assert R.pick_variant(8192, 8) == "tile"                # prefill workload
     assert R.pick_variant(8192, 8, "stream") == "stream"
     assert R.pick_variant(128, 8, "tile") == "tile"
@@ -244,8 +249,12 @@ def test_contract_sizes_and_variant_queries():
     # few experts, every group within one 64-token streaming pass: streaming
     # even above 32 rows per expert on average
     assert R.pick_variant(384, 8, max_group_rows=58) == "stream"     # E=8, 48 rows per expert
-    assert R.pick_variant(384, 8, max_group_rows=65) == "tile"       # a group needs two passes
-    assert R.pick_variant(384, 8) == "tile"                          # largest group unknown
+    assert R.pick_variant(384, 8, max_group_rows=128) == "stream"    # 8 experts, 48 rows, one block each
+    assert R.pick_variant(384, 8, max_group_rows=129) == "tile"      # a group needs two blocks
+    assert R.pick_variant(448, 8, max_group_rows=64) == "stream"     # 56 rows, one pass each
+    assert R.pick_variant(448, 8, max_group_rows=70) == "tile"
+    assert R.pick_variant(576, 9, max_group_rows=65) == "tile"       # a group needs two passes
+    assert R.pick_variant(576, 9) == "tile"                          # largest group unknown
     assert R.pick_variant(1280, 32, max_group_rows=54) == "stream"   # E=32, 40 rows per expert
     assert R.pick_variant(2560, 64, max_group_rows=54) == "tile"     # more than 32 experts
 

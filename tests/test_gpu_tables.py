@@ -102,7 +102,7 @@ def test_validator_on_workload_tables():
             assert int(v.item()) > 0, (name, which)
 
 
-@pytest.mark.parametrize("T,E", [(75, 5), (128, 8), (130, 8), (200, 8), (600, 8)])
+@pytest.mark.parametrize("T,E", [(75, 5), (128, 8), (192, 8), (193, 8), (144, 9), (145, 9), (600, 8)])
 def test_stage_entries_agree_with_forward(T, E):
     """gate_up then down, each under AUTO, equal the forward with the family
     rmoe_pick_variant names, bit for bit (E=5 with 150 pairs is the batch on
