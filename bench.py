@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--dense-compare", action="store_true",
                     help="only time the tiled stages on one expert (a dense SwiGLU FFN) beside "
                          "torch's fp16 matmul on the same GEMM shapes")
+    ap.add_argument("--phase-timing", default="",
+                    help="only report where the tiled stages' time goes, per phase of their work "
+                         "items, for these comma-separated workloads (dense = one expert, 8192 "
+                         "tokens, H=4096, I=14336), with the phase-timing diagnostic library")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), the "
                          "reference that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
@@ -476,8 +480,86 @@ def dense_compare(reps=20):
                       "vendor_gemm_down_tflops": round(f2 / mm2 / 1e6, 1)}), flush=True)
 
 
+def phase_timing(names, reps=3):
+    """Where the tiled stages' time goes, from the phase-timing build of the
+    library (librmoe_phase.so: the same kernels, bit-identical results, four
+    shader-clock reads per work item; include/routed_moe_phase.h).  For each
+    workload and stage (tiled family, one launch at a time): the shares of
+    the workgroups' summed run time spent in item prologues (until the first
+    K step's operands have landed), K loops, epilogues (until the last output
+    store is issued) and between items; the idle tail, 1 - mean / max of the
+    workgroups' run times (workgroups that ran out of items while others
+    still work); the items per workgroup; and the shader clock, the longest
+    workgroup run in ticks over the launch time.  Medians over ``reps``
+    launches."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routed_grouped_amd as R
+    import workloads
+    R.use_library(R.PHASE_LIB_PATH)
+    dev = torch.device("cuda:0")
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    for name in names:
+        if name == "dense":
+            cfg = workloads.Config("dense", 8192, 1, 1, 4096, 14336)
+            inp = workloads.make_inputs(cfg, device=dev, topk_ids=np.zeros((8192, 1), np.int32))
+        else:
+            cfg = workloads.CONFIGS[name]
+            inp = workloads.make_inputs(cfg, device=dev)
+        c = R.build_contract(inp.topk_ids, cfg.experts)
+        gs, go, gpo, gidx = (i32(c[q]) for q in ("group_sizes", "group_offsets",
+                                                 "group_padded_offsets", "group_idx_for_bx"))
+        Tp = c["total_padded_tokens"]
+        stacked = torch.zeros((Tp, cfg.hidden), dtype=torch.float16, device=dev)
+        wc = torch.zeros(max(c["pairs"], 1), dtype=torch.float32, device=dev)
+        R.pack(inp.x.to(dev), torch.from_numpy(inp.topk_w.reshape(-1).copy()).to(dev),
+               i32(c["padded_row_of_pair"]), i32(c["compact_pos_of_pair"]), stacked, wc)
+        hid = torch.empty((Tp, cfg.intermediate), dtype=torch.float16, device=dev)
+        out = torch.empty((Tp, cfg.hidden), dtype=torch.float16, device=dev)
+        stages = (("gate_up", 0, lambda: R.gate_up(stacked, inp.wg, inp.wu, gs, gpo, gidx, hid,
+                                                  c["pairs"], variant="tile")),
+                  ("down", 1, lambda: R.down(hid, inp.wd, wc, gs, go, gpo, gidx, out,
+                                             variant="tile")))
+        for stage, idx, fn in stages:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            runs = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3
+                rec = R.phase_cycles()[idx].astype(np.float64)
+                ran = rec[:, 3] > 0
+                pro, loop, epi, items, whole = (rec[ran, j] for j in range(5))
+                tot = whole.sum()
+                runs.append({"us": us, "prologue": pro.sum() / tot, "k_loop": loop.sum() / tot,
+                             "epilogue": epi.sum() / tot,
+                             "between_items": (tot - pro.sum() - loop.sum() - epi.sum()) / tot,
+                             "idle_tail": 1.0 - whole.mean() / whole.max(),
+                             "clock_ghz": float(whole.max()) / us / 1e3,
+                             "items_min": int(items.min()), "items_max": int(items.max()),
+                             "workgroups": int(ran.sum())})
+            med = {k: statistics.median(r[k] for r in runs) for k in runs[0]}
+            print(json.dumps({"phase_timing": name, "stage": stage, "launch_us": round(med["us"], 1),
+                              **{k: round(med[k], 4) for k in ("prologue", "k_loop", "epilogue",
+                                                               "between_items", "idle_tail")},
+                              "clock_ghz": round(med["clock_ghz"], 3),
+                              "items_per_workgroup": [runs[0]["items_min"], runs[0]["items_max"]],
+                              "workgroups": runs[0]["workgroups"]}), flush=True)
+        del inp, stacked, hid, out
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.phase_timing:
+        phase_timing(args.phase_timing.split(","))
+        return
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib, args.steps)
         return

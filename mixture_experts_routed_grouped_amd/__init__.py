@@ -20,6 +20,8 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librmoe.so")
+# diagnostic build: the same library with the tiled kernels' phase timing
+PHASE_LIB_PATH = os.path.join(_PKG, "librmoe_phase.so")
 
 VARIANT_AUTO, VARIANT_STREAM, VARIANT_TILE = 0, 1, 2
 _VARIANTS = {"auto": 0, "stream": 1, "tile": 2, 0: 0, 1: 1, 2: 2}
@@ -80,6 +82,32 @@ def lib():
             fn.restype = res
         _lib = L
     return _lib
+
+
+def use_library(path: str) -> str:
+    """Load the library at ``path`` for every later call (for instance
+    PHASE_LIB_PATH, the phase-timing diagnostic build); returns the path that
+    was in use.  Buffers and streams stay valid across the switch."""
+    global _lib, LIB_PATH
+    prev = LIB_PATH
+    LIB_PATH, _lib = path, None
+    lib()
+    return prev
+
+
+def phase_cycles():
+    """The phase-timing records of the last tiled launches
+    (rmoe_phase_cycles; only the diagnostic library exports it): uint64
+    [2 stages (gate/up, down), RMOE_PHASE_WG workgroups, 5] = prologue,
+    K loop, epilogue, items, whole run, in shader-clock ticks."""
+    L = lib()
+    if not hasattr(L, "rmoe_phase_cycles"):
+        raise RmoeError(f"{LIB_PATH} is not the phase-timing build ({PHASE_LIB_PATH})")
+    fn = L.rmoe_phase_cycles
+    fn.argtypes, fn.restype = [_P, ctypes.c_size_t], ctypes.c_int
+    out = np.zeros((2, 1024, 5), dtype=np.uint64)
+    _check(fn(_np_ptr(out), out.nbytes), "rmoe_phase_cycles")
+    return out
 
 
 def status_str(status: int) -> str:

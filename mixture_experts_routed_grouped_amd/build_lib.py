@@ -1,9 +1,12 @@
 """Build librmoe.so (the C-ABI library) in-tree with hipcc for gfx950.
 
 Every source is compiled to an object in parallel, then linked into
-``mixture_experts_routed_grouped_amd/librmoe.so``.  Run as a script, or call
-``build()``; ``RMOE_RESOURCE_USAGE=1`` prints each kernel's register, LDS and
-spill usage from the compiler.
+``mixture_experts_routed_grouped_amd/librmoe.so``.  The tiled kernels'
+source is compiled a second time with ``RMOE_PHASE_TIMING=1`` and linked
+with the same other objects into the diagnostic ``librmoe_phase.so``
+(include/routed_moe_phase.h).  Run as a script, or call ``build()``;
+``RMOE_RESOURCE_USAGE=1`` prints each kernel's register, LDS and spill usage
+from the compiler.
 """
 from __future__ import annotations
 
@@ -16,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librmoe.so")
+PHASE_LIB = os.path.join(PKG, "librmoe_phase.so")
 SOURCES = ["rmoe_api.cpp", "rmoe_stream.hip", "rmoe_tile.hip", "rmoe_pack.hip", "rmoe_contract.hip", "rmoe_router.hip"]
 ARCH = "gfx950"
 
@@ -37,11 +41,14 @@ def build(verbose: bool = False) -> str:
     extra = ["-Rpass-analysis=kernel-resource-usage"] if os.environ.get("RMOE_RESOURCE_USAGE") else []
     procs = []
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
+    phase_obj = os.path.join(BUILD, "rmoe_tile_phase.o")
+    jobs = [(src, os.path.join(BUILD, os.path.splitext(src)[0] + ".o"), []) for src in SOURCES]
+    jobs.append(("rmoe_tile.hip", phase_obj, ["-DRMOE_PHASE_TIMING=1"]))
+    for src, obj, defs in jobs:
+        if not defs:
+            objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON, *extra, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -57,10 +64,12 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed on {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    phase_objs = [phase_obj if o.endswith("rmoe_tile.o") else o for o in objs]
+    for out, link in ((LIB, objs), (PHASE_LIB, phase_objs)):
+        tmp = out + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *link, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
     return LIB
 
 

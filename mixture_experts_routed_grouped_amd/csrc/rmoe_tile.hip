@@ -74,6 +74,34 @@ __device__ __forceinline__ void dma16_sb(const void *base, unsigned off, unsigne
                  : "memory", "m0");
 }
 
+// ---- Phase timing, compiled only into the diagnostic library
+//      (RMOE_PHASE_TIMING=1: librmoe_phase.so).  Each workgroup of a
+//      persistent launch sums the shader-clock ticks (s_memtime) that its
+//      items spend in their prologue (addresses, the first DMAs until step 0
+//      has landed), their K loop and their epilogue (until the last output
+//      store is issued), and writes the three sums, its item count and its
+//      whole run time to phase_cycles[stage][workgroup] (stage 0 gate/up,
+//      1 down); rmoe_phase_cycles copies them to the host.  Wave 0 keeps the
+//      record: its token half always holds rows.  The instrumentation adds
+//      four clock reads per item and leaves every result unchanged.
+#ifndef RMOE_PHASE_TIMING
+#define RMOE_PHASE_TIMING 0
+#endif
+constexpr int kPhaseWg = 1024;  // workgroups recorded per stage
+struct PhaseSums {
+    unsigned long long pro = 0, loop = 0, epi = 0, items = 0;
+};
+__device__ __forceinline__ unsigned long long phase_clock() {
+#if RMOE_PHASE_TIMING
+    return __builtin_amdgcn_s_memtime();
+#else
+    return 0;
+#endif
+}
+#if RMOE_PHASE_TIMING
+__device__ unsigned long long phase_cycles[2][kPhaseWg][5];
+#endif
+
 // One tile: blocks bx (b0: its expert, offset in the group, valid rows) and
 // bx+1 (rows1 valid rows; has1: it belongs to the same expert) against the
 // weight slice nt.  Called with the workgroup's LDS; leaves no DMA in flight.
@@ -82,7 +110,10 @@ __device__ __forceinline__ void dma16_sb(const void *base, unsigned off, unsigne
 // write-back; the single-launch path hands the hidden rows over this way.
 template <bool DUAL, bool WT = false>
 __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem, int nt, int bx,
-                                         const BlockInfo &b0, bool has1, int rows1) {
+                                         const BlockInfo &b0, bool has1, int rows1,
+                                         PhaseSums *ps = nullptr) {
+    const unsigned long long t0 = phase_clock();
+    unsigned long long t1 = t0, t2 = t0;
     const int rows0 = b0.rows;
     const int64_t K = a.K, N = a.N;
     // opaque per tile: keeps the compiler from hoisting per-lane address
@@ -232,6 +263,7 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
         for (int d = 0; d < DPS; ++d) dma_g(-1, d);
         wait_vm<DMA_HALF + DPS>();  // step 0 landed: only weights 1 and that part may be in flight
         bar();
+        if constexpr (RMOE_PHASE_TIMING) t1 = phase_clock();
         if constexpr (NTT > 0) {
 #pragma unroll
             for (int i = 0; i < NRD; ++i) read_one(smem, smem + NWS * SLOT, 0, 0, i);
@@ -259,13 +291,28 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
         case 1: kloop(std::integral_constant<int, 1>{}); break;
         default: kloop(std::integral_constant<int, 0>{}); break;
     }
+    if constexpr (RMOE_PHASE_TIMING) t2 = phase_clock();
+    auto phase_end = [&]() {
+        if constexpr (RMOE_PHASE_TIMING) {
+            if (ps) {
+                const unsigned long long t3 = phase_clock();
+                ps->pro += t1 - t0;
+                ps->loop += t2 - t1;
+                ps->epi += t3 - t2;
+                ps->items += 1;
+            }
+        }
+    };
     // ---- epilogue, staged through LDS so that the global stores are whole
     //      128-byte lines (the MFMA layout gives a lane one token and 4
     //      consecutive features: 8 bytes in each of 32 rows per store).  No
     //      barrier: a wave stages only into its own 8 KB piece of the slots,
     //      which only its own DMAs (all landed: it waited for them) fill, and
     //      no wave reads the ring after the last K-step barrier.
-    if (ntt == 0) return;
+    if (ntt == 0) {
+        phase_end();
+        return;
+    }
     const int bmine = bx + wt;
     const int toff = b0.token_offset + kBlockM * wt;
     // staged tile of this wave: 128 token rows x OB bytes (gate/up: 64
@@ -343,6 +390,7 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
                 *(h8 *)(ybase + (int64_t)row * N + 8 * c) = v;
         }
     }
+    phase_end();
 }
 
 // Runs work item it (rmoe_sched.h) with the workgroup's LDS.  The item list
@@ -351,14 +399,15 @@ __device__ __forceinline__ void run_tile(const StageArgs &a, unsigned char *smem
 // the streaming family applies per block, in block_info), so both families
 // act on the same table and skip the same blocks of a corrupted one.
 template <bool DUAL, bool WT = false>
-__device__ __forceinline__ void run_item(const StageArgs &a, unsigned char *smem, const TileItem &it) {
+__device__ __forceinline__ void run_item(const StageArgs &a, unsigned char *smem, const TileItem &it,
+                                         PhaseSums *ps = nullptr) {
     BlockInfo b0;
     b0.e = it.e;
     b0.token_offset = it.off;
     b0.rows = a.gidx[it.bx] == it.e ? it.rows0 : 0;
     const int rows1 = (it.rows1 > 0 && a.gidx[it.bx + 1] == it.e) ? it.rows1 : 0;
     if (b0.rows == 0 && rows1 == 0) return;
-    run_tile<DUAL, WT>(a, smem, it.nt, it.bx, b0, rows1 > 0, rows1);
+    run_tile<DUAL, WT>(a, smem, it.nt, it.bx, b0, rows1 > 0, rows1, ps);
 }
 
 // Persistent kernel: one workgroup per CU (a multiple of 8 of them, LDS_BYTES
@@ -374,7 +423,21 @@ __global__ __launch_bounds__(256) void tile_kernel(StageArgs a, int NT) {
     const TileSeq seq = tile_seq(a.gs, a.E, NT, blockIdx.x % kXcd, kXcd);
     const int nl = gridDim.x / kXcd;
     TileCursor cur;
-    for (int i = blockIdx.x / kXcd; i < seq.n; i += nl) run_item<DUAL>(a, smem, tile_item(a.gs, a.gpo, seq, i, cur));
+    PhaseSums ps;
+    [[maybe_unused]] const unsigned long long ts = phase_clock();
+    for (int i = blockIdx.x / kXcd; i < seq.n; i += nl)
+        run_item<DUAL>(a, smem, tile_item(a.gs, a.gpo, seq, i, cur), &ps);
+#if RMOE_PHASE_TIMING
+    const unsigned long long te = phase_clock();
+    if (threadIdx.x == 0 && blockIdx.x < kPhaseWg) {
+        unsigned long long *g = phase_cycles[DUAL ? 0 : 1][blockIdx.x];
+        g[0] = ps.pro;
+        g[1] = ps.loop;
+        g[2] = ps.epi;
+        g[3] = ps.items;
+        g[4] = te - ts;
+    }
+#endif
 }
 
 // ---- Both stages in one launch.
@@ -638,3 +701,15 @@ hipError_t launch_fused(const StageArgs &gu, const StageArgs &dn, int32_t *sync,
 }
 
 }  // namespace rmoe
+
+#if RMOE_PHASE_TIMING
+#include "../../include/routed_moe_phase.h"
+
+int rmoe_phase_cycles(uint64_t *cycles, size_t bytes) {
+    if (!cycles || bytes < sizeof(rmoe::phase_cycles)) return RMOE_ERR_INVALID_ARGUMENT;
+    return hipMemcpyFromSymbol(cycles, HIP_SYMBOL(rmoe::phase_cycles), sizeof(rmoe::phase_cycles), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess
+               ? RMOE_OK
+               : RMOE_ERR_LAUNCH;
+}
+#endif
