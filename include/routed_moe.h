@@ -310,7 +310,9 @@ RMOE_API int rmoe_down_f16(const void *workspace, const void *down_w,
  * for p < num_tokens*top_k.  x [num_tokens, H] fp16 device, topk_weights
  * [num_tokens*top_k] fp32 device, maps int32 device, stacked [Tp, H] fp16
  * device, w_compact [pairs] fp32 device.  Other rows of stacked are not
- * written.  H must be a multiple of 8.  A pair whose padded row lies outside
+ * written.  H must be a multiple of 8, at most 2^33 (RMOE_ERR_UNSUPPORTED_
+ * SHAPE otherwise).  Each token row is read once and written to its top_k
+ * packed rows.  A pair whose padded row lies outside
  * [0, total_padded_tokens) or whose compact position lies outside [0, pairs)
  * (the device contract marks pairs with invalid expert ids with -1) moves
  * nothing.
@@ -324,8 +326,9 @@ RMOE_API int rmoe_pack_f16(const void *x, const float *topk_weights,
  * Combine (same write-up, section 2.7 item 7: the scatter-reduce of the k
  * expert outputs of each token): y[t] = fp16( sum_j out[padded_row_of_pair
  * [t*top_k + j]] ) with the sum in fp32 in slot order j = 0..top_k-1.
- * out [Tp, H] fp16 device, y [num_tokens, H] fp16 device.  H multiple of 8.
- * Slots whose padded row lies outside [0, total_padded_tokens) add nothing.
+ * out [Tp, H] fp16 device, y [num_tokens, H] fp16 device.  H a multiple of
+ * 8, at most 2^33 (RMOE_ERR_UNSUPPORTED_SHAPE otherwise).  Slots whose padded
+ * row lies outside [0, total_padded_tokens) add nothing.
  */
 RMOE_API int rmoe_combine_f16(const void *out, const int32_t *padded_row_of_pair,
                               int64_t num_tokens, int32_t top_k, int64_t hidden, void *y,

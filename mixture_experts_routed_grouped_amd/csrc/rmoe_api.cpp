@@ -416,7 +416,7 @@ int rmoe_pack_f16(const void *x, const float *topk_weights, const int32_t *prow,
                   void *stacked, float *w_compact, int64_t total_padded_tokens, void *stream) {
     if (num_tokens < 0 || top_k < 0 || hidden <= 0 || total_padded_tokens < 0)
         return RMOE_ERR_INVALID_ARGUMENT;
-    if (hidden % 8 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    if (hidden % 8 != 0 || hidden / 8 > ((int64_t)1 << 30)) return RMOE_ERR_UNSUPPORTED_SHAPE;
     const int64_t pairs = num_tokens * top_k;
     if (pairs == 0) return RMOE_OK;
     if (!x || !topk_weights || !prow || !cpos || !stacked || !w_compact)
@@ -434,7 +434,7 @@ int rmoe_combine_f16(const void *out, const int32_t *prow, int64_t num_tokens, i
                      int64_t hidden, void *y, int64_t total_padded_tokens, void *stream) {
     if (num_tokens < 0 || top_k < 0 || hidden <= 0 || total_padded_tokens < 0)
         return RMOE_ERR_INVALID_ARGUMENT;
-    if (hidden % 8 != 0) return RMOE_ERR_UNSUPPORTED_SHAPE;
+    if (hidden % 8 != 0 || hidden / 8 > ((int64_t)1 << 30)) return RMOE_ERR_UNSUPPORTED_SHAPE;
     if (num_tokens == 0) return RMOE_OK;
     if (!y || (top_k > 0 && (!out || !prow))) return RMOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(y) || !aligned16(out) || !aligned4(prow)) return RMOE_ERR_MISALIGNED;

@@ -133,6 +133,9 @@ def test_argument_errors_without_gpu():
     assert L.rmoe_down_f16(*([fake] * 8), 256, 128, 4, 640, -3, 5, 0, None) == -1
     assert L.rmoe_pack_f16(fake, fake, fake, fake, 3, 2, 12, fake, fake, 640, None) == -2
     assert L.rmoe_combine_f16(fake, fake, -1, 2, 16, fake, 640, None) == -1
+    huge = 8 * ((1 << 30) + 1)  # rows beyond 2^30 16-byte chunks
+    assert L.rmoe_pack_f16(fake, fake, fake, fake, 3, 2, huge, fake, fake, 640, None) == -2
+    assert L.rmoe_combine_f16(fake, fake, 3, 2, huge, fake, 640, None) == -2
     assert L.rmoe_workspace_bytes(640, 128) == 640 * 128 * 2
     assert R.status_str(-5).startswith("tables violate")
 
