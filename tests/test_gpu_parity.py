@@ -166,6 +166,46 @@ def test_pack_and_combine():
     assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16))
 
 
+@pytest.mark.parametrize("T,k,E,H", [
+    (100, 12, 16, 64),     # top_k above the lanes per token row (8 chunks): weights in two passes
+    (300, 1, 3, 8),        # one chunk per row: 256 tokens per workgroup, a ragged last pass
+    (77, 4, 9, 16384),     # 2048 chunks per row: two chunk batches per thread
+    (150, 8, 20, 7168),    # the large workload's row length (896 chunks, a partial last batch)
+])
+def test_pack_and_combine_row_shapes(T, k, E, H):
+    """Pack at every row shape of the token-major kernel: each packed row,
+    every routed weight and the untouched padding rows against the oracle's
+    pack; combine of a random routed output against the oracle's combine,
+    all bit for bit."""
+    from _gpu_run import SENTINEL
+    rng = np.random.default_rng(T * 7 + k)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float16))
+    tw = rng.random(T * k).astype(np.float32)
+    oc = C.build_contract(ids.tolist(), E)
+    xs, wc = C.pack_rows(oc, list(x.numpy()), list(tw), np.zeros(H, np.float16))
+    prow = np.asarray(oc["padded_row_of_pair"])
+    Tp, pairs = oc["total_padded_tokens"], oc["pairs"]
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    stacked = torch.full((Tp, H), SENTINEL, dtype=torch.int16, device="cuda").view(torch.float16)
+    w_compact = torch.zeros(pairs, dtype=torch.float32, device="cuda")
+    print(f"[pack] T={T} k={k} E={E} H={H}: {pairs} pairs into {Tp} rows", flush=True)
+    R.pack(x.cuda(), torch.from_numpy(tw).cuda(), i32(prow), i32(oc["compact_pos_of_pair"]), stacked,
+           w_compact)
+    out = torch.from_numpy(rng.standard_normal((Tp, H)).astype(np.float16)).cuda()
+    y = torch.empty((T, H), dtype=torch.float16, device="cuda")
+    R.combine(out, i32(prow), k, y)
+    torch.cuda.synchronize()
+    got = stacked.cpu().numpy().view(np.uint16)
+    valid = np.zeros(Tp, dtype=bool)
+    valid[prow] = True
+    assert np.array_equal(got[valid], np.asarray(xs)[valid].view(np.uint16))
+    assert (got[~valid] == np.uint16(SENTINEL)).all()
+    assert np.array_equal(w_compact.cpu().numpy(), np.asarray(wc, np.float32))
+    want = CB.combine(out.cpu().numpy(), prow, T, k)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
 # ------------------------------------------------------------ full size
 def _block_sample(c, seed=0):
     """Pairs to hold against the oracle at full size: one row of every block
