@@ -115,12 +115,16 @@ def test_single_expert_and_no_pairs(variant):
     _full_compare(workloads.make_inputs(cfg, topk_ids=ids), variant)
 
 
-@pytest.mark.parametrize("T,E,k", [(128, 8, 2), (96, 6, 2)])
-def test_auto_mid_batch(T, E, k):
-    """25-32 routed rows per expert on average: the automatic choice streams
-    with 64-token passes (two MFMA token tiles per pass)."""
-    cfg = workloads.Config(f"mid{T}", T, E, k, 512, 1024, routing="uniform", seed=12)
-    _full_compare(workloads.make_inputs(cfg), "auto")
+@pytest.mark.parametrize("T,E,k,routing", [(128, 8, 2, "uniform"), (96, 6, 2, "uniform"),
+                                           (192, 8, 2, "uniform"), (176, 8, 2, "zipf")])
+def test_auto_mid_batch(T, E, k, routing):
+    """25-32 routed rows per expert on average, and up to 48 with at most 8
+    experts: the automatic choice streams with 64-token passes (two MFMA
+    token tiles per pass; groups above 64 rows take a second pass)."""
+    cfg = workloads.Config(f"mid{T}", T, E, k, 512, 1024, routing=routing, zipf_s=1.2, seed=12)
+    inp = workloads.make_inputs(cfg)
+    assert R.pick_variant(T * k, E) == "stream"
+    _full_compare(inp, "auto")
 
 
 def test_determinism():
