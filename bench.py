@@ -354,26 +354,30 @@ def measure(cfg, variant, steps, warmup, with_aux=False):
 
 
 # token counts of the crossover sweep, per (E, top_k, H, I, Zipf s or None
-# for uniform routing): skewed routing at decode-to-mid batch sizes on the
-# shapes of the workloads, and uniform routing with few experts at 24-80
-# rows per expert
+# for uniform routing): decode-to-mid batch sizes on the shapes of the
+# workloads and on few-expert shapes, each on both sides of the family
+# thresholds (16-112 rows per expert)
 CROSSOVER = {
-    "E128_k8_H7168_I2048_zipf1.2": (128, 8, 7168, 2048, 1.2, [16, 32, 64, 128, 256, 512]),
-    "E64_k6_H2048_I1408_zipf1.1": (64, 6, 2048, 1408, 1.1, [32, 64, 128, 192, 256, 384, 512]),
-    "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 224, 256]),
-    "E8_k2_H4096_I14336_uniform": (8, 2, 4096, 14336, None, [96, 128, 160, 192, 224, 256, 320]),
-    "E8_k2_H6144_I16384_uniform": (8, 2, 6144, 16384, None, [128, 160, 192, 224, 256]),
-    "E8_k2_H2048_I5632_uniform": (8, 2, 2048, 5632, None, [128, 160, 192, 224, 256]),
-    "E4_k2_H4096_I14336_uniform": (4, 2, 4096, 14336, None, [64, 80, 96, 112, 128]),
-    "E16_k2_H4096_I14336_uniform": (16, 2, 4096, 14336, None, [192, 256, 320, 384, 448, 512, 640]),
-    "E32_k4_H4096_I2048_uniform": (32, 4, 4096, 2048, None, [192, 256, 320, 384, 448, 512, 640]),
+    "E128_k8_H7168_I2048_zipf1.2": (128, 8, 7168, 2048, 1.2, [16, 64, 128, 256, 384, 512, 640]),
+    "E128_k8_H7168_I2048_uniform": (128, 8, 7168, 2048, None, [256, 384, 512, 640]),
+    "E64_k6_H2048_I1408_zipf1.1": (64, 6, 2048, 1408, 1.1, [32, 128, 256, 384, 512, 768]),
+    "E64_k6_H2048_I1408_uniform": (64, 6, 2048, 1408, None, [256, 320, 384, 448, 512]),
+    "E32_k4_H4096_I2048_zipf1.2": (32, 4, 4096, 2048, 1.2, [256, 384, 512, 768]),
+    "E32_k4_H4096_I2048_uniform": (32, 4, 4096, 2048, None, [256, 320, 384, 448, 512]),
+    "E16_k2_H4096_I14336_zipf1.2": (16, 2, 4096, 14336, 1.2, [192, 256, 320, 384]),
+    "E16_k2_H4096_I14336_uniform": (16, 2, 4096, 14336, None, [256, 320, 384, 448, 512]),
+    "E8_k2_H4096_I14336_zipf1.2": (8, 2, 4096, 14336, 1.2, [64, 128, 192, 224, 256, 288]),
+    "E8_k2_H4096_I14336_uniform": (8, 2, 4096, 14336, None, [64, 128, 192, 224, 256, 288, 320, 352, 384]),
+    "E8_k2_H6144_I16384_uniform": (8, 2, 6144, 16384, None, [192, 224, 256, 288, 320]),
+    "E8_k2_H2048_I5632_uniform": (8, 2, 2048, 5632, None, [192, 256, 320, 384, 448]),
+    "E4_k2_H4096_I14336_uniform": (4, 2, 4096, 14336, None, [96, 128, 160, 192, 224]),
 }
 
 
 def crossover_sweep(reps=20):
-    """Forward time of both kernel families across batch sizes under Zipf
-    routing (one JSON line per batch), with the family the library picks
-    from the average alone and from the average and the largest group."""
+    """Forward time of both kernel families across batch sizes under uniform
+    and Zipf routing (one JSON line per batch), with the family the library
+    picks from the average alone and from the average and the largest group."""
     import numpy as np
     import torch
 

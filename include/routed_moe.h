@@ -162,18 +162,20 @@ RMOE_API int rmoe_contract_sizes(int64_t num_pairs, int32_t num_experts, int32_t
 /*
  * The kernel family for a batch: `variant` itself if it is
  * RMOE_VARIANT_STREAM or _TILE; for RMOE_VARIANT_AUTO, streaming while the
- * batch averages at most 32 routed rows per expert (there an expert's GEMM
- * is bound by reading its weights, as the contract tutorial's closing note
- * says of small M), or at most 48 with at most 8 experts (the tiled family
- * then has few work items), and, when max_group_rows >= 0 (the largest group size,
- * known to a caller that holds host tables), while every expert fits one
- * 128-row block -- under skewed routing the largest experts' blocks would
- * otherwise take several streaming passes, each reading their weights
- * again -- and tiling otherwise.  With max_group_rows known it also
- * streams batches of at most 32 experts whose every group fits one
- * 64-token streaming pass (each weight byte is then read once, while the
- * tiled family has too few work items to fill the GPU), whatever their
- * average.  max_group_rows < 0 means unknown: the
+ * batch averages few routed rows per expert -- there an expert's GEMM is
+ * bound by reading its weights, as the contract tutorial's closing note
+ * says of small M: at most 96 rows with at most 4 experts, 56 with at most
+ * 8 (the tiled family then has few work items), 32 below 32 experts and 36
+ * from 32 experts -- and tiling otherwise.  When max_group_rows >= 0 (the
+ * largest group size, known to a caller that holds host tables): with fewer
+ * than 32 experts streaming also needs every expert to fit one 128-row
+ * block (under skewed routing a larger group's blocks read its weights once
+ * per block, which weighs on a batch of few experts); and batches of at
+ * most 32 experts stream whatever their average while every group fits one
+ * streaming pass -- the largest group at most 64 rows, or at most 96 at an
+ * average of at most 80 rows (at most 8 experts) or 48 (each weight byte is
+ * then read once, while the tiled family has too few work items).
+ * max_group_rows < 0 means unknown: the
  * forward, rmoe_gate_up_f16 and rmoe_down_f16 never read device tables,
  * so their AUTO is this function with max_group_rows = -1 (the two stages
  * of one batch therefore always agree); pass the family this returns as

@@ -17,9 +17,6 @@ constexpr int64_t B = RMOE_BLOCK_M;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 constexpr int32_t kMaxDeviceExperts = 8192;  // the device contract keeps per-expert tables in LDS
-#ifndef RMOE_STREAM_MAX_ROWS
-#define RMOE_STREAM_MAX_ROWS 32  // average rows per expert up to which AUTO streams
-#endif
 // default bound on how long a fused down tile waits for its pair's hidden
 // rows (the longest real wait is one gate/up stage: milliseconds)
 constexpr int64_t kFusedWaitUs = 2000000;
@@ -42,52 +39,57 @@ int check_dims(int64_t hidden, int64_t intermediate, int32_t num_experts,
 
 // Kernel family: the weight-streaming family when experts hold few rows on
 // average (then a weight byte serves a handful of tokens and the stage is
-// HBM-bound), the LDS-tiled family otherwise.  Streaming passes take 32
-// tokens per pass up to kStreamOneTile rows per expert and 64 beyond, so
-// that blocks of up to 64 rows read their weights once.  Measured crossover
-// (uniform routing): about 48 rows per expert for E=8 (H=4096, I=14336),
-// 40 for E=64 (2048, 1408), 28 for E=128 (7168, 2048); at 32 streaming
-// wins or ties within 2% on all three.
-// Under skewed (Zipf) routing the crossover moves lower -- about 12-16 rows
-// per expert for E=128, 18-24 for E=64 -- because the largest experts'
-// blocks need several streaming passes, each reading their weights again.
-// So when the caller knows the largest group (max_group_rows >= 0, from
-// host tables), streaming is kept only while every expert fits one block
-// (<= 128 rows, at most two 64-token passes).
-// The largest group also widens the streaming range for few experts: when
-// every expert fits one 64-token pass, each weight byte is read exactly
-// once, while the tiled family has too few work items to fill the GPU
-// (E=8, H=4096: 128 down-stage items for 256 CUs).  Measured, uniform
-// routing: E=8 (4096, 14336) streams 18-22% faster at 40-48 rows per
-// expert, E=32 (4096, 2048) 4-16% at 40 (two boxes); E=16 within 4% either way;
-// for E=64 and E=128 tiling wins from about 30-40 rows, so the wider range
-// stops at 32 experts.
-// With at most 8 experts the average threshold is 48 rows: the tiled family
-// then has few work items (E=8, H=4096 gives its down stage 128 items for
-// 256 CUs).  Measured at 48 rows per expert, streaming takes less time on
-// every such batch: E=8 (4096, 14336) uniform 19% less and Zipf 1.2 2%,
-// E=8 (6144, 16384) 2.5%, E=8 (2048, 5632) 38%, E=4 (4096, 14336) 41%; at
-// 56 the two larger E=8 batches (Zipf, and 6144 x 16384) tile in 6-8% less.
-constexpr int64_t kStreamMaxRowsPerExpert = RMOE_STREAM_MAX_ROWS;
-constexpr int32_t kFewExperts = 8;
-constexpr int64_t kStreamMaxRowsFewExperts = 48;
+// HBM-bound), the LDS-tiled family otherwise.  A streaming block takes the
+// narrowest pass of 32, 64 or 96 tokens that holds its rows (96 then 32 for
+// 97-128 rows), so blocks of up to 96 rows read their weights once; a group
+// of g rows reads its expert's weights about g/64 times beyond that.
+//
+// Average threshold by expert count, from forward times of both families
+// (one MI355X, uniform and Zipf routing, 16-112 rows per expert):
+//   E <= 4: 96 rows -- the tiled family has very few work items (E=4,
+//     H=4096: 64 down-stage items for 256 CUs); E=4 (4096, 14336) streams
+//     14-42% faster at 48-96, tiles 13-14% faster at 112;
+//   E <= 8: 56 -- at 56, E=8 (4096, 14336) streams 15% faster (uniform) and
+//     1-4% (Zipf 1.2), (6144, 16384) 1-4%; at 64 the Zipf batch tiles 9%
+//     faster;
+//   E < 32: 32 -- E=16 (4096, 14336) tiles up to 5% faster at 40-48
+//     uniform, 7% from 40 under Zipf;
+//   E >= 32: 36 -- E=64 (2048, 1408) streams 2-4% faster at 36 and tiles
+//     2% faster at 42; E=128 (7168, 2048) tiles 4-6% faster at 40 (E=32
+//     (4096, 2048) streams faster up to 64 rows, 18% at 40).
+// When the caller knows the largest group (max_group_rows >= 0, from host
+// tables):
+//   * with fewer than 32 experts streaming also needs every group to fit
+//     one 128-row block: the few experts' extra weight reads then weigh on
+//     the whole batch (E=16 Zipf 1.2, 40 rows per expert, largest group 197:
+//     tiling 7% faster).  With 32 or more experts the extra reads of the
+//     large groups are a small share (E=128 Zipf 1.2 at 8-32 rows, largest
+//     group 120-485: streaming 2-18% faster; E=64 Zipf 1.1 at 24-36,
+//     largest 219-330: 4-9%);
+//   * batches of at most 32 experts whose every group fits one pass stream
+//     whatever their average while the largest group is at most 64 rows,
+//     and up to 96 rows at an average of at most 80 (E <= 8) or 48 rows:
+//     each weight byte is then read once, while the tiled family has too
+//     few work items (E=8 (4096, 14336) at 64-80 rows, largest 75-94:
+//     streaming 5-15% faster, (2048, 5632) 41-52%, (6144, 16384) between
+//     2% faster and 8% slower; E=32 (4096, 2048) at 40-48, largest 57-72:
+//     14-18% faster; E=16 (4096, 14336) at 40-48, largest 51-62: within 5%
+//     either way).
 constexpr int64_t kStreamMaxGroupRows = B;
-constexpr int64_t kStreamOnePassRows = 64;
-constexpr int32_t kStreamOnePassMaxExperts = 32;
-constexpr int64_t kStreamOneTile = 24;
+constexpr int32_t kManyExperts = 32;
+int64_t stream_max_avg_rows(int32_t num_experts) {
+    return num_experts <= 4 ? 96 : num_experts <= 8 ? 56 : num_experts < kManyExperts ? 32 : 36;
+}
 int pick_variant(int32_t variant, int64_t pairs, int32_t num_experts, int64_t max_group_rows = -1) {
     if (variant == RMOE_VARIANT_STREAM || variant == RMOE_VARIANT_TILE) return variant;
-    const bool few = pairs <= kStreamMaxRowsPerExpert * (int64_t)num_experts ||
-                     (num_experts <= kFewExperts && pairs <= kStreamMaxRowsFewExperts * (int64_t)num_experts);
-    const bool fits = max_group_rows < 0 || max_group_rows <= kStreamMaxGroupRows;
-    const bool one_pass = max_group_rows >= 0 && max_group_rows <= kStreamOnePassRows &&
-                          num_experts <= kStreamOnePassMaxExperts;
+    const int32_t E = num_experts;
+    const bool few = pairs <= stream_max_avg_rows(E) * (int64_t)E;
+    const bool fits = max_group_rows < 0 || max_group_rows <= kStreamMaxGroupRows || E >= kManyExperts;
+    const bool one_pass =
+        max_group_rows >= 0 && E <= kManyExperts &&
+        (max_group_rows <= 64 || (max_group_rows <= 96 && pairs <= (E <= 8 ? 80 : 48) * (int64_t)E));
     return (few && fits) || one_pass ? RMOE_VARIANT_STREAM : RMOE_VARIANT_TILE;
 }
-int stream_tiles(int64_t pairs, int32_t num_experts) {
-    return pairs <= kStreamOneTile * (int64_t)num_experts ? 1 : 2;
-}
-
 int to_status(hipError_t e) { return e == hipSuccess ? RMOE_OK : RMOE_ERR_LAUNCH; }
 
 // Hand-over of the single launch.  AUTO hands hidden rows across XCDs: the
@@ -119,7 +121,7 @@ int gate_up_impl(const void *x, const void *gate_w, const void *up_w, const int3
     if (M == 0) return RMOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
-        return to_status(rmoe::launch_stream_gate_up(a, stream_tiles(pairs, E), s));
+        return to_status(rmoe::launch_stream_gate_up(a, s));
     return to_status(rmoe::launch_tile_gate_up(a, s));
 }
 
@@ -145,7 +147,7 @@ int down_impl(const void *workspace, const void *down_w, const float *rw, const 
     if (M == 0) return RMOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pick_variant(variant, pairs, E) == RMOE_VARIANT_STREAM)
-        return to_status(rmoe::launch_stream_down(a, stream_tiles(pairs, E), s));
+        return to_status(rmoe::launch_stream_down(a, s));
     return to_status(rmoe::launch_tile_down(a, s));
 }
 

@@ -44,9 +44,8 @@ struct StageArgs {
 };
 
 // Kernel-family launchers; return hipSuccess or the launch error.
-// tiles: 32-token tiles per streaming pass (1 or 2)
-hipError_t launch_stream_gate_up(const StageArgs &a, int tiles, hipStream_t s);
-hipError_t launch_stream_down(const StageArgs &a, int tiles, hipStream_t s);
+hipError_t launch_stream_gate_up(const StageArgs &a, hipStream_t s);
+hipError_t launch_stream_down(const StageArgs &a, hipStream_t s);
 hipError_t launch_tile_gate_up(const StageArgs &a, hipStream_t s);
 hipError_t launch_tile_down(const StageArgs &a, hipStream_t s);
 // Both tiled stages in one persistent launch (gu.y = dn.x = the hidden

@@ -18,11 +18,12 @@
 //     instruction) reaches ~4 TB/s.  Each wave owns a ring of
 //     D chunk slots, refilled D-1 chunks ahead; MFMA operands come back out
 //     of LDS with swizzled, conflict-free ds_read_b128;
-//   * the pass's tokens (one 32-token MFMA tile, or two for blocks of up
-//     to 64 rows) ride in the same slots (tokens are shared by all
-//     workgroups of the block and come from L2), so every global read is a
-//     DMA and the only waits are the explicit vmcnt ones; a block with more
-//     rows than a pass holds takes several passes, each reading the weights;
+//   * the pass's tokens (one to three 32-token MFMA tiles: the narrowest
+//     pass that holds the block's rows, up to 96) ride in the same slots
+//     (tokens are shared by all workgroups of the block and come from L2),
+//     so every global read is a DMA and the only waits are the explicit
+//     vmcnt ones; a block of 97-128 rows takes a 96-token pass and a
+//     32-token one, reading its weights twice;
 //   * weights are the MFMA A operand (v_mfma_f32_32x32x16_f16, 32 feature
 //     rows), tokens the B operand; a lane ends up with 4 consecutive
 //     features of one token, so stores are 8-byte fp16 quads;
@@ -67,9 +68,9 @@ constexpr int MF = 32;                // output features per workgroup (MFMA row
 constexpr int CK = 64;                // K per chunk: one 128-byte line per weight row
 constexpr int CHUNK_B = MF * CK * 2;  // 4 KB: one matrix's chunk
 
-// TT: 32-token tiles per pass.  TT = 1 for decode-shaped blocks (~16 rows);
-// TT = 2 for blocks of up to 64 rows, which then read the weights once
-// instead of once per 32-token tile.
+// TT: 32-token tiles per pass: 1, 2 or 3 (96 tokens, the largest pass the
+// 160 KB of LDS holds); a block takes the narrowest pass that holds its rows,
+// so it reads its weights once instead of once per 32-token tile.
 template <bool DUAL, int KS, int D, int TT>
 struct StreamCfg {
     static constexpr int FT = DUAL ? (TT == 1 ? RMOE_GU_FT1 : 1) : (TT == 1 ? RMOE_DN_FT1 : RMOE_DN_FT2);
@@ -225,8 +226,13 @@ __device__ __forceinline__ void stream_pass(const StageArgs &a, const BlockInfo 
     __syncthreads();  // the next pass refills the ring that holds red[]
 }
 
-// grid: (N / (32 FT), num_blocks_m); block: 64 * KS threads; dynamic LDS LDS_BYTES.
-template <bool DUAL, int KS, int D, int TT>
+// grid: (N / (32 FT), num_blocks_m); block: 64 * KS threads; dynamic LDS: the
+// largest pass's.  Each block is run in the fewest passes the LDS allows, so
+// that its expert's weights are read once up to 96 rows: one pass of 32, 64
+// or 96 tokens, or for 97-128 rows a 96-token pass and a 32-token one.  Token
+// rows are moved in groups of 8 (16 for the wider passes, at most 8 rows past
+// the valid ones and never past the block).
+template <bool DUAL, int KS, int D>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int bx = blockIdx.y;
@@ -236,49 +242,58 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(StageArgs a) {
     // loop bounds in scalar registers (uniform branches)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int n0 = blockIdx.x * MF * StreamCfg<DUAL, KS, D, TT>::FT;
-    for (int p0 = 0; p0 < bi.rows; p0 += 32 * TT) {
-        // token DMA rows of this pass, in 8s
-        const int td = (min(bi.rows - p0, 32 * TT) + 7) / 8;
-        if constexpr (TT == 1) {
-            switch (td) {
-                case 1: stream_pass<DUAL, KS, D, 1, 1>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                case 2: stream_pass<DUAL, KS, D, 1, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                case 3: stream_pass<DUAL, KS, D, 1, 3>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                default: stream_pass<DUAL, KS, D, 1, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
-            }
-        } else {
-            switch ((td + 1) / 2) {  // in 16s: fewer instances, at most 8 extra rows moved
-                case 1: stream_pass<DUAL, KS, D, 2, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                case 2: stream_pass<DUAL, KS, D, 2, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                case 3: stream_pass<DUAL, KS, D, 2, 6>(a, bi, bx, p0, n0, smem, wave, lane); break;
-                default: stream_pass<DUAL, KS, D, 2, 8>(a, bi, bx, p0, n0, smem, wave, lane); break;
-            }
+    const int n0 = blockIdx.x * MF * StreamCfg<DUAL, KS, D, 1>::FT;
+    int p0 = 0;
+    if (bi.rows > 96) {
+        stream_pass<DUAL, KS, D, 3, 12>(a, bi, bx, 0, n0, smem, wave, lane);
+        p0 = 96;
+    }
+    const int rem = bi.rows - p0;
+    const int td = (rem + 7) / 8;  // token rows of the last pass, in 8s
+    if (rem <= 32) {
+        switch (td) {
+            case 1: stream_pass<DUAL, KS, D, 1, 1>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            case 2: stream_pass<DUAL, KS, D, 1, 2>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            case 3: stream_pass<DUAL, KS, D, 1, 3>(a, bi, bx, p0, n0, smem, wave, lane); break;
+            default: stream_pass<DUAL, KS, D, 1, 4>(a, bi, bx, p0, n0, smem, wave, lane); break;
         }
+    } else if (rem <= 64) {
+        if (td <= 6)
+            stream_pass<DUAL, KS, D, 2, 6>(a, bi, bx, p0, n0, smem, wave, lane);
+        else
+            stream_pass<DUAL, KS, D, 2, 8>(a, bi, bx, p0, n0, smem, wave, lane);
+    } else {
+        if (td <= 10)
+            stream_pass<DUAL, KS, D, 3, 10>(a, bi, bx, p0, n0, smem, wave, lane);
+        else
+            stream_pass<DUAL, KS, D, 3, 12>(a, bi, bx, p0, n0, smem, wave, lane);
     }
 }
 
-template <bool DUAL, int KS, int D, int TT>
+template <bool DUAL, int KS, int D>
 hipError_t launch(const StageArgs &a, hipStream_t s) {
-    using C = StreamCfg<DUAL, KS, D, TT>;
+    using C1 = StreamCfg<DUAL, KS, D, 1>;
+    using C2 = StreamCfg<DUAL, KS, D, 2>;
+    using C3 = StreamCfg<DUAL, KS, D, 3>;
+    static_assert(C1::FT == C2::FT && C2::FT == C3::FT, "one grid for every pass width");
+    constexpr int lds = C3::LDS_BYTES > C2::LDS_BYTES ? (C3::LDS_BYTES > C1::LDS_BYTES ? C3::LDS_BYTES : C1::LDS_BYTES)
+                                                       : (C2::LDS_BYTES > C1::LDS_BYTES ? C2::LDS_BYTES : C1::LDS_BYTES);
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D, TT>, C::LDS_BYTES, lds_set);
+    hipError_t e = lds_opt_in_once((const void *)stream_kernel<DUAL, KS, D>, lds, lds_set);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(a.N / (MF * C::FT)), (unsigned)a.M);
-    hipLaunchKernelGGL((stream_kernel<DUAL, KS, D, TT>), grid, dim3(64 * KS), C::LDS_BYTES, s, a);
+    dim3 grid((unsigned)(a.N / (MF * C1::FT)), (unsigned)a.M);
+    hipLaunchKernelGGL((stream_kernel<DUAL, KS, D>), grid, dim3(64 * KS), lds, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_stream_gate_up(const StageArgs &a, int tiles, hipStream_t s) {
-    return tiles == 2 ? launch<true, RMOE_GU_KS, RMOE_GU_D, 2>(a, s)
-                      : launch<true, RMOE_GU_KS, RMOE_GU_D, 1>(a, s);
+hipError_t launch_stream_gate_up(const StageArgs &a, hipStream_t s) {
+    return launch<true, RMOE_GU_KS, RMOE_GU_D>(a, s);
 }
 
-hipError_t launch_stream_down(const StageArgs &a, int tiles, hipStream_t s) {
-    return tiles == 2 ? launch<false, RMOE_DN_KS, RMOE_DN_D, 2>(a, s)
-                      : launch<false, RMOE_DN_KS, RMOE_DN_D, 1>(a, s);
+hipError_t launch_stream_down(const StageArgs &a, hipStream_t s) {
+    return launch<false, RMOE_DN_KS, RMOE_DN_D>(a, s);
 }
 
 }  // namespace rmoe

@@ -227,15 +227,20 @@ def test_contract_sizes_and_variant_queries():
     assert L.rmoe_contract_sizes(10, 0, None, None) == -1
     assert L.rmoe_contract_sizes(2 ** 31, 4, None, None) == -1
     assert L.rmoe_contract_sizes(10, 4, None, None) == 0    # outputs are optional
-    # streaming while the batch averages at most 32 rows per expert (48 with
-    # at most 8 experts), tiles above
+    # streaming while the batch averages at most 96 rows per expert with at
+    # most 4 experts, 56 with at most 8, 32 below 32 experts and 36 from 32
+    # experts, tiling above
     assert R.pick_variant(128, 8) == "stream"               # decode workload
     assert R.pick_variant(288, 9) == "stream"
     assert R.pick_variant(289, 9) == "tile"
-    assert R.pick_variant(384, 8) == "stream"
-    assert R.pick_variant(385, 8) == "tile"
-    assert R.pick_variant(192, 4) == "stream"
-    assert R.pick_variant(193, 4) == "tile"
+    assert R.pick_variant(448, 8) == "stream"
+    assert R.pick_variant(449, 8) == "tile"
+    assert R.pick_variant(384, 4) == "stream"
+    assert R.pick_variant(385, 4) == "tile"
+    assert R.pick_variant(992, 31) == "stream"
+    assert R.pick_variant(993, 31) == "tile"
+    assert R.pick_variant(1152, 32) == "stream"
+    assert R.pick_variant(1153, 32) == "tile"
     assert R.pick_variant(8192, 8) == "tile"                # prefill workload
     assert R.pick_variant(8192, 8, "stream") == "stream"
     assert R.pick_variant(128, 8, "tile") == "tile"
@@ -243,23 +248,40 @@ def test_contract_sizes_and_variant_queries():
     assert L.rmoe_pick_variant(0, -1, 4, -1) == -1
     assert L.rmoe_pick_variant(0, 10, 0, -1) == -1
     assert L.rmoe_pick_variant(0, 10, 4, 11) == -1        # a group larger than the batch
-    # the largest group weighs in when known: every expert must fit one block
-    assert R.pick_variant(2048, 128, max_group_rows=120) == "stream"
-    assert R.pick_variant(2048, 128, max_group_rows=242) == "tile"   # Zipf 1.2, 256 tokens
+    # the largest group weighs in when known: below 32 experts every expert
+    # must fit one block
     assert R.pick_variant(128, 8, max_group_rows=23) == "stream"     # decode workload
     assert R.pick_variant(4096, 8, max_group_rows=100) == "tile"     # the average decides first
-    assert R.pick_variant(2048, 128, "stream", max_group_rows=242) == "stream"
-    # few experts, every group within one 64-token streaming pass: streaming
-    # even above 32 rows per expert on average
-    assert R.pick_variant(384, 8, max_group_rows=58) == "stream"     # E=8, 48 rows per expert
     assert R.pick_variant(384, 8, max_group_rows=128) == "stream"    # 8 experts, 48 rows, one block each
     assert R.pick_variant(384, 8, max_group_rows=129) == "tile"      # a group needs two blocks
+    assert R.pick_variant(512, 16, max_group_rows=162) == "tile"     # E=16 Zipf, 32 rows per expert
+    assert R.pick_variant(512, 16) == "stream"                       # largest group unknown
+    # from 32 experts on the large groups' extra weight reads are a small share
+    assert R.pick_variant(2048, 128, max_group_rows=120) == "stream"
+    assert R.pick_variant(2048, 128, max_group_rows=242) == "stream"  # Zipf 1.2, 256 tokens
+    assert R.pick_variant(2304, 64, max_group_rows=330) == "stream"   # Zipf 1.1, 384 tokens
+    assert R.pick_variant(2305, 64, max_group_rows=54) == "tile"      # above 36 rows per expert
+    assert R.pick_variant(5120, 128, max_group_rows=608) == "tile"    # Zipf 1.2, 640 tokens
+    assert R.pick_variant(1024, 32, max_group_rows=208) == "stream"   # Zipf 1.2, 256 tokens
+    assert R.pick_variant(2048, 128, "tile", max_group_rows=120) == "tile"
+    # at most 32 experts, every group within one streaming pass: streaming
+    # above the average threshold (largest group up to 64 rows; up to 96 at
+    # an average of at most 80 rows with at most 8 experts, else 48)
     assert R.pick_variant(448, 8, max_group_rows=64) == "stream"     # 56 rows, one pass each
-    assert R.pick_variant(448, 8, max_group_rows=70) == "tile"
-    assert R.pick_variant(576, 9, max_group_rows=65) == "tile"       # a group needs two passes
+    assert R.pick_variant(512, 8, max_group_rows=75) == "stream"     # 64 rows, largest 75
+    assert R.pick_variant(512, 8, max_group_rows=96) == "stream"
+    assert R.pick_variant(512, 8, max_group_rows=97) == "tile"       # a group needs two passes
+    assert R.pick_variant(640, 8, max_group_rows=94) == "stream"     # 80 rows, largest 94
+    assert R.pick_variant(648, 8, max_group_rows=96) == "tile"       # 81 rows per expert
+    assert R.pick_variant(1280, 32, max_group_rows=57) == "stream"   # E=32, 40 rows per expert
+    assert R.pick_variant(1536, 32, max_group_rows=72) == "stream"   # E=32, 48 rows per expert
+    assert R.pick_variant(1537, 32, max_group_rows=72) == "tile"
+    assert R.pick_variant(720, 16, max_group_rows=64) == "stream"    # 45 rows, largest 64
+    assert R.pick_variant(720, 16, max_group_rows=65) == "stream"    # 45 rows, largest 65 (<= 48 on average)
+    assert R.pick_variant(784, 16, max_group_rows=65) == "tile"      # 49 rows, largest 65
+    assert R.pick_variant(576, 9, max_group_rows=65) == "tile"       # 64 rows with 9 experts
     assert R.pick_variant(576, 9) == "tile"                          # largest group unknown
-    assert R.pick_variant(1280, 32, max_group_rows=54) == "stream"   # E=32, 40 rows per expert
-    assert R.pick_variant(2560, 64, max_group_rows=54) == "tile"     # more than 32 experts
+    assert R.pick_variant(2560, 33, max_group_rows=64) == "tile"     # more than 32 experts
 
 
 def test_validate_device_argument_errors_without_gpu():

@@ -115,6 +115,22 @@ def test_single_expert_and_no_pairs(variant):
     _full_compare(workloads.make_inputs(cfg, topk_ids=ids), variant)
 
 
+def test_stream_pass_widths():
+    """Every pass plan of the streaming kernels, one block per expert: 1-32
+    rows (one 32-token pass moving 1-4 groups of 8 rows), 33-64 (one
+    64-token pass, 5-6 or 7-8 groups), 65-96 (one 96-token pass, 9-10 or
+    11-12 groups) and 97-128 (a 96-token pass, then a 32-token one with 1-32
+    rows), each on the edges of its row groups; then a uniform k=2 batch of
+    about 85 rows per expert.  Compared with the oracle whole."""
+    sizes = [1, 9, 17, 25, 32, 33, 48, 49, 64, 65, 80, 81, 96, 97, 105, 113, 121, 128]
+    ids = np.concatenate([np.full(n, e, np.int32) for e, n in enumerate(sizes)])[:, None]
+    ids = np.random.default_rng(3).permutation(ids)
+    cfg = workloads.Config("passes", len(ids), len(sizes), 1, 256, 256, seed=15)
+    _full_compare(workloads.make_inputs(cfg, topk_ids=ids), "stream")
+    cfg = workloads.Config("passes_u", 170, 4, 2, 512, 384, routing="uniform", seed=16)
+    _full_compare(workloads.make_inputs(cfg), "stream")
+
+
 @pytest.mark.parametrize("T,E,k,routing", [(128, 8, 2, "uniform"), (96, 6, 2, "uniform"),
                                            (192, 8, 2, "uniform"), (176, 8, 2, "zipf")])
 def test_auto_mid_batch(T, E, k, routing):
