@@ -10,9 +10,10 @@
 //      group_sizes, group_offsets and group_padded_offsets (padded size of
 //      an expert with c pairs: ceil((c+1)/128)*128);
 //   3. scatter: every chunk walks its pairs 256 at a time in pair order; a
-//      pair's rank among the earlier pairs of its expert in the same 256 is
-//      counted directly, so the sort is stable (ascending pair index inside
-//      an expert) and the tables are unique;
+//      pair's rank among the earlier pairs of its expert in its wave comes
+//      from one ballot per bit of the expert id, and the four waves take
+//      their positions in pair order, so the sort is stable (ascending pair
+//      index inside an expert) and the tables are unique;
 //   4. blocks: group_idx_for_bx[bx] = the last expert whose padded start is
 //      <= bx*128 (binary search over the strictly increasing starts).
 // Pairs whose expert id lies outside [0, E) are left out of every table,
@@ -56,6 +57,73 @@ namespace {
 constexpr int TPB = 256;
 constexpr int CHUNK = 2048;  // pairs per chunk
 constexpr int SMALL_E = 1024;  // expert bound of the one-launch path (its LDS)
+constexpr int NWAVE = TPB / 64;
+
+// Exclusive scans of two per-thread values over the workgroup, in thread
+// order (shuffles within each wave, then the wave totals); also the totals.
+// Integer sums: exact, whatever the order.  Every thread must call it.
+__device__ __forceinline__ void block_scan2(int32_t c, int32_t p, int32_t &exc_c, int32_t &exc_p,
+                                            int32_t &tot_c, int32_t &tot_p, int32_t *wsum_c,
+                                            int32_t *wsum_p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t ic = c, ip = p;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t tc = __shfl_up(ic, d), tp = __shfl_up(ip, d);
+        if (lane >= d) {
+            ic += tc;
+            ip += tp;
+        }
+    }
+    if (lane == 63) {
+        wsum_c[wave] = ic;
+        wsum_p[wave] = ip;
+    }
+    __syncthreads();
+    exc_c = ic - c;
+    exc_p = ip - p;
+    tot_c = 0;
+    tot_p = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        if (w < wave) {
+            exc_c += wsum_c[w];
+            exc_p += wsum_p[w];
+        }
+        tot_c += wsum_c[w];
+        tot_p += wsum_p[w];
+    }
+    __syncthreads();  // wsum_* may be reused
+}
+
+// Stable placement of 256 consecutive pairs (one per thread, in pair order;
+// valid = its expert e lies in [0, E)): the lanes of a wave holding the same
+// expert are found with one ballot per bit of the expert id (a lane keeps
+// the lanes whose bit agrees with its own, bit after bit), which gives the
+// pair's rank among the earlier pairs of its expert in its wave; then the
+// waves take their positions from next[] in pair order and advance it.
+// Returns the compact position, or -1 for an invalid pair.  Every thread
+// must call it (nbits: bits of E - 1, uniform).
+__device__ __forceinline__ int32_t place_pairs(int32_t e, bool valid, int nbits, int32_t *next) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const uint64_t m = __ballot(set);
+        same &= set ? m : ~m;
+    }
+    const int rank = __popcll(same & below), cnt = __popcll(same);
+    int32_t pos = -1;
+    for (int w = 0; w < NWAVE; ++w) {
+        if (wave == w && valid) {
+            pos = next[e] + rank;
+            if (rank == cnt - 1) next[e] = pos + 1;  // after every lane of the wave read next[e]
+        }
+        __syncthreads();
+    }
+    return pos;
+}
 
 __global__ __launch_bounds__(TPB) void hist_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                    int32_t E, int32_t *__restrict__ cc,
@@ -82,18 +150,29 @@ __global__ __launch_bounds__(TPB) void scan_kernel(int32_t *__restrict__ cc,
                                                    int32_t *__restrict__ go, int32_t *__restrict__ gpo,
                                                    int32_t *__restrict__ bad) {
     extern __shared__ int32_t cnt[];
-    __shared__ int32_t part_c[TPB], part_p[TPB];
-    // per expert: exclusive scan over the chunks, in place; total -> gs
+    __shared__ int32_t wsum_c[NWAVE], wsum_p[NWAVE];
+    // per expert: exclusive scan over the chunks, in place; total -> gs.
+    // Counts are read 8 chunks at a time, so the loads of a group overlap.
     for (int e = threadIdx.x; e < E; e += TPB) {
         int32_t run = 0;
-        for (int c = 0; c < nch; ++c) {
-            const int32_t v = cc[(int64_t)c * E + e];
-            cc[(int64_t)c * E + e] = run;
-            run += v;
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = c0 + j < nch ? cc[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < nch) {
+                    cc[(int64_t)(c0 + j) * E + e] = run;
+                    run += v[j];
+                }
+            }
         }
         cnt[e] = run;
         gs[e] = run;
     }
+    // out-of-range pairs of every chunk
+    int32_t nb = 0;
+    for (int c = threadIdx.x; c < nch; c += TPB) nb += bad_c[c];
     __syncthreads();
     // exclusive scans over the experts: each thread a contiguous segment
     const int seg = (E + TPB - 1) / TPB;
@@ -103,26 +182,14 @@ __global__ __launch_bounds__(TPB) void scan_kernel(int32_t *__restrict__ cc,
         sc += cnt[e];
         sp += (cnt[e] / kBlockM + 1) * kBlockM;  // ceil((c+1)/128)*128
     }
-    part_c[threadIdx.x] = sc;
-    part_p[threadIdx.x] = sp;
-    __syncthreads();
+    int32_t rc, rp, tc, tp, xb, xd, tb, td;
+    block_scan2(sc, sp, rc, rp, tc, tp, wsum_c, wsum_p);
+    block_scan2(nb, 0, xb, xd, tb, td, wsum_c, wsum_p);  // tb: the out-of-range total
     if (threadIdx.x == 0) {
-        int32_t rc = 0, rp = 0;
-        for (int i = 0; i < TPB; ++i) {
-            const int32_t vc = part_c[i], vp = part_p[i];
-            part_c[i] = rc;
-            part_p[i] = rp;
-            rc += vc;
-            rp += vp;
-        }
-        go[E] = rc;
-        gpo[E] = rp;
-        int32_t nb = 0;
-        for (int c = 0; c < nch; ++c) nb += bad_c[c];
-        *bad = nb;
+        go[E] = tc;
+        gpo[E] = tp;
+        *bad = tb;
     }
-    __syncthreads();
-    int32_t rc = part_c[threadIdx.x], rp = part_p[threadIdx.x];
     for (int e = e0; e < e1; ++e) {
         go[e] = rc;
         gpo[e] = rp;
@@ -139,7 +206,7 @@ __global__ __launch_bounds__(TPB) void scatter_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ prow,
                                                       int32_t *__restrict__ cpos) {
     extern __shared__ int32_t base[];  // [E] next compact position per expert
-    __shared__ int32_t eid[TPB];
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int e = threadIdx.x; e < E; e += TPB) base[e] = go[e] + cc[(int64_t)blockIdx.x * E + e];
     __syncthreads();
     const int64_t c0 = (int64_t)blockIdx.x * CHUNK;
@@ -147,19 +214,7 @@ __global__ __launch_bounds__(TPB) void scatter_kernel(const int32_t *__restrict_
         const int64_t p = c0 + sub + threadIdx.x;
         const int32_t e = p < pairs ? ids[p] : -1;
         const bool valid = e >= 0 && e < E;
-        eid[threadIdx.x] = valid ? e : -1;
-        __syncthreads();
-        int32_t rank = 0, tot = 0, pos = -1;
-        if (valid) {
-            for (int j = 0; j < TPB; ++j) {
-                const bool same = eid[j] == e;
-                rank += (same && j < (int)threadIdx.x) ? 1 : 0;
-                tot += same ? 1 : 0;
-            }
-            pos = base[e] + rank;
-        }
-        __syncthreads();  // every pair read base[] before it moves on
-        if (valid && rank == tot - 1) base[e] += tot;
+        const int32_t pos = place_pairs(e, valid, nbits, base);
         if (p < pairs) {
             if (valid) {
                 order[pos] = (int32_t)p;
@@ -170,7 +225,6 @@ __global__ __launch_bounds__(TPB) void scatter_kernel(const int32_t *__restrict_
                 prow[p] = -1;
             }
         }
-        __syncthreads();  // eid[] and base[] are reused by the next 256 pairs
     }
 }
 
@@ -204,7 +258,7 @@ __global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__re
                                                              int32_t *__restrict__ bad) {
     __shared__ int32_t h[SMALL_E + 1];    // counts (+ out-of-range), then next position
     __shared__ int32_t lgo[SMALL_E + 1], lgpo[SMALL_E + 1];
-    __shared__ int32_t part_c[TPB], part_p[TPB], eid[TPB];
+    __shared__ int32_t wsum_c[NWAVE], wsum_p[NWAVE];
     // 1. histogram
     for (int e = threadIdx.x; e <= E; e += TPB) h[e] = 0;
     __syncthreads();
@@ -213,7 +267,8 @@ __global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__re
         atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
     }
     __syncthreads();
-    // 2. totals and the two exclusive scans over the experts
+    // 2. totals and the two exclusive scans over the experts: each thread
+    //    sums a contiguous run of experts, then a scan across the threads
     const int seg = (E + TPB - 1) / TPB;
     const int e0 = min(E, (int)threadIdx.x * seg), e1 = min(E, e0 + seg);
     int32_t sc = 0, sp = 0;
@@ -222,53 +277,29 @@ __global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__re
         sc += h[e];
         sp += (h[e] / kBlockM + 1) * kBlockM;  // ceil((c+1)/128)*128
     }
-    part_c[threadIdx.x] = sc;
-    part_p[threadIdx.x] = sp;
-    __syncthreads();
+    int32_t rc, rp, tc, tp;
+    block_scan2(sc, sp, rc, rp, tc, tp, wsum_c, wsum_p);
     if (threadIdx.x == 0) {
-        int32_t rc = 0, rp = 0;
-        for (int i = 0; i < TPB; ++i) {
-            const int32_t vc = part_c[i], vp = part_p[i];
-            part_c[i] = rc;
-            part_p[i] = rp;
-            rc += vc;
-            rp += vp;
-        }
-        go[E] = lgo[E] = rc;
-        gpo[E] = lgpo[E] = rp;
+        go[E] = lgo[E] = tc;
+        gpo[E] = lgpo[E] = tp;
         *bad = h[E];
     }
-    __syncthreads();
-    {
-        int32_t rc = part_c[threadIdx.x], rp = part_p[threadIdx.x];
-        for (int e = e0; e < e1; ++e) {
-            go[e] = lgo[e] = rc;
-            gpo[e] = lgpo[e] = rp;
-            rc += h[e];
-            rp += (h[e] / kBlockM + 1) * kBlockM;
-        }
+    for (int e = e0; e < e1; ++e) {
+        go[e] = lgo[e] = rc;
+        gpo[e] = lgpo[e] = rp;
+        rc += h[e];
+        rp += (h[e] / kBlockM + 1) * kBlockM;
     }
     __syncthreads();  // every count was read: h[] becomes the next compact position
     for (int e = threadIdx.x; e < E; e += TPB) h[e] = lgo[e];
     __syncthreads();
     // 3. stable scatter, 256 pairs at a time in pair order
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int sub = 0; sub < pairs; sub += TPB) {
         const int p = sub + threadIdx.x;
         const int32_t e = p < pairs ? ids[p] : -1;
         const bool valid = e >= 0 && e < E;
-        eid[threadIdx.x] = valid ? e : -1;
-        __syncthreads();
-        int32_t rank = 0, tot = 0, pos = -1;
-        if (valid) {
-            for (int j = 0; j < TPB; ++j) {
-                const bool same = eid[j] == e;
-                rank += (same && j < (int)threadIdx.x) ? 1 : 0;
-                tot += same ? 1 : 0;
-            }
-            pos = h[e] + rank;
-        }
-        __syncthreads();  // every pair read h[] before it moves on
-        if (valid && rank == tot - 1) h[e] += tot;
+        const int32_t pos = place_pairs(e, valid, nbits, h);
         if (p < pairs) {
             if (valid) {
                 order[pos] = p;
@@ -279,7 +310,6 @@ __global__ __launch_bounds__(TPB) void small_contract_kernel(const int32_t *__re
                 prow[p] = -1;
             }
         }
-        __syncthreads();  // eid[] and h[] are reused by the next 256 pairs
     }
     // 4. block -> expert: the last expert whose padded start is <= bx*128
     for (int bx = threadIdx.x; bx < M; bx += TPB) {

@@ -9,7 +9,12 @@
 // 4-stage ring (one barrier per chunk); v_mfma_f32_32x32x16_f16 with gate
 // rows as A and a 32-token tile as B, fp32 logits.  TOK = 64: 4 waves = 2
 // token halves x 2 interleaved sets of 32-expert tiles; TOK = 32: one token
-// tile, 4 interleaved sets of expert tiles.  TOK = 32 gives twice the
+// tile, 4 interleaved sets of expert tiles -- or, with fewer than four
+// expert tiles (E <= 64), the waves also split each chunk's four K-steps
+// (E <= 32: one K-step per wave; E <= 64: two), so that every wave has work
+// and a chunk costs one or two dependent MFMAs instead of four (64 tokens,
+// E = 8, H = 4096: two workgroups of 64 chunks); their partial logits are
+// added in a fixed order.  TOK = 32 gives twice the
 // workgroups, i.e. more memory streams per CU, for batches that would not
 // fill the chip twice over (16384 tokens, H = 7168, E = 128: 197 -> 100 us).
 // The logits go through LDS; 4 lanes per token then take the row maximum,
@@ -36,9 +41,11 @@ struct RouterCfg {
     static constexpr int NT = EP / 32;            // 32-expert tiles
     static constexpr int EW = TOK == 64 ? 2 : 4;  // waves sharing the expert tiles
     static constexpr int TPW = (NT + EW - 1) / EW;  // tiles per wave
+    // waves per expert tile that split a chunk's 4 K-steps (TOK = 32 only)
+    static constexpr int KSW = TOK == 32 && NT == 1 ? 4 : TOK == 32 && NT == 2 ? 2 : 1;
     static constexpr int LDS_BYTES = RT_NST * STAGE;  // >= the TROWS x EP fp32 logits
     static_assert(TOK == 64 || TOK == 32, "tokens per workgroup: whole 32-token tiles");
-    static_assert(LDS_BYTES >= TROWS * EP * 4, "logits fit in the ring");
+    static_assert(LDS_BYTES >= KSW * TROWS * EP * 4, "partial logits fit in the ring");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -59,7 +66,10 @@ __global__ __launch_bounds__(256) void router_kernel(const _Float16 *__restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     // token tile of this wave, and its first expert tile (then every EW-th)
-    const int th = TOK == 64 ? (wave & 1) : 0, eh = TOK == 64 ? (wave >> 1) : wave;
+    // (with KSW > 1: expert tile wave % NT, K-steps s with s % KSW == ks)
+    const int ks = C::KSW > 1 ? wave / C::NT : 0;
+    const int th = TOK == 64 ? (wave & 1) : 0;
+    const int eh = TOK == 64 ? (wave >> 1) : C::KSW > 1 ? wave % C::NT : wave;
 
     // DMA sources: instruction j = wave*NIW + i moves rows 8j .. 8j+7 of the
     // chunk (rows < TOK: tokens, clamped to the last token; the rest: gate
@@ -106,6 +116,7 @@ __global__ __launch_bounds__(256) void router_kernel(const _Float16 *__restrict_
         const unsigned char *base = smem + (kc % RT_NST) * C::STAGE;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            if (s % C::KSW != ks) continue;
             const h8 b = *(const h8 *)(base + lds_off(32 * th + lr, 2 * s + lh));
 #pragma unroll
             for (int t = 0; t < C::TPW; ++t) {
@@ -120,8 +131,10 @@ __global__ __launch_bounds__(256) void router_kernel(const _Float16 *__restrict_
     wait_vm<0>();
     bar();
 
-    // ---- logits -> LDS [TROWS tokens][EP experts] fp32.  32x32 accumulator
-    //      layout: register 4q + r holds expert row 8q + 4lh + r, token lr.
+    // ---- logits -> LDS [TROWS tokens][EP experts] fp32 (partial logits of
+    //      K-split ks at L + ks * TROWS * EP, then added in order of ks).
+    //      32x32 accumulator layout: register 4q + r holds expert row
+    //      8q + 4lh + r, token lr.
     float *L = reinterpret_cast<float *>(smem);
 #pragma unroll
     for (int t = 0; t < C::TPW; ++t) {
@@ -131,10 +144,19 @@ __global__ __launch_bounds__(256) void router_kernel(const _Float16 *__restrict_
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    L[(32 * th + lr) * EP + 32 * et + 8 * q + 4 * lh + r] = acc[t][4 * q + r];
+                    L[ks * C::TROWS * EP + (32 * th + lr) * EP + 32 * et + 8 * q + 4 * lh + r] = acc[t][4 * q + r];
         }
     }
     __syncthreads();
+    if constexpr (C::KSW > 1) {
+        for (int i = tid; i < C::TROWS * EP; i += 256) {
+            float v = L[i];
+#pragma unroll
+            for (int j = 1; j < C::KSW; ++j) v += L[j * C::TROWS * EP + i];
+            L[i] = v;
+        }
+        __syncthreads();
+    }
 
     // ---- softmax and top-k: 4 consecutive lanes per token, lane `sub` owns
     //      experts sub, sub + 4, ...

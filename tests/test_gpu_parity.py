@@ -344,6 +344,37 @@ def test_full_size(name):
     print(f"[full-size] {name}: {len(pairs)} rows within tolerance, rel RMS {rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("name,cfg", [
+    ("large-shape Zipf, 384 tokens", workloads.Config("zipf_e128", 384, 128, 8, 7168, 2048,
+                                                      routing="zipf", zipf_s=1.2, seed=21)),
+    ("fine-shape Zipf, 384 tokens", workloads.Config("zipf_e64", 384, 64, 6, 2048, 1408,
+                                                     routing="zipf", zipf_s=1.1, seed=22)),
+])
+def test_stream_skewed_mid_batch(name, cfg):
+    """Streaming on the workloads' shapes under skew, where AUTO streams with
+    the largest group known although that group spans several blocks (one
+    96-token pass then a 32-token one per full block): padding rows
+    untouched, every valid row written and finite, one row of every live
+    block (plus each expert's first and last row) against the oracle."""
+    inp = workloads.make_inputs(cfg, device="cuda")
+    d = prepare(inp)
+    gs = np.asarray(d["c"]["group_sizes"])
+    assert gs.max() > 256                                    # a group of three or more blocks
+    assert R.pick_variant(d["c"]["pairs"], cfg.experts, max_group_rows=int(gs.max())) == "stream"
+    print(f"[stream-skew] {name}: forward, largest group {int(gs.max())}", flush=True)
+    forward(d, "stream")
+    mask = valid_row_mask(d)
+    assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
+    _all_valid_rows_written(d)
+    pairs, blocks = _block_sample(d["c"], seed=5)
+    print(f"[stream-skew] {name}: oracle on {len(pairs)} rows ({blocks} live blocks)", flush=True)
+    o_hid, o_out = _oracle_rows(inp, pairs)
+    rows = d["prow"][torch.tensor(pairs, device="cuda")].long()
+    rel = _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(), o_hid, o_out,
+                         name)
+    print(f"[stream-skew] {name}: {len(pairs)} rows within tolerance, rel RMS {rel:.2e}", flush=True)
+
+
 def test_pack_large_batch_nontemporal_path():
     """The large workload packs 1.9 GB of rows, above the size where pack
     stores them non-temporally: sampled rows equal their token's row bit for
