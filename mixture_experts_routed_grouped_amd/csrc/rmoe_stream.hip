@@ -32,8 +32,6 @@
 //
 // Blocks with no valid row exit at once, so the tail blocks and the slack
 // block of a full group touch no weight.
-#include <type_traits>
-
 #include "rmoe_device.h"
 #include "rmoe_internal.h"
 
@@ -49,17 +47,6 @@
 #ifndef RMOE_DN_D
 #define RMOE_DN_D 2
 #endif
-// 32-feature weight tiles per workgroup, by stage and pass width (the
-// 64-token pass of gate/up has no LDS room for a second tile)
-#ifndef RMOE_GU_FT1
-#define RMOE_GU_FT1 1
-#endif
-#ifndef RMOE_DN_FT1
-#define RMOE_DN_FT1 2
-#endif
-#ifndef RMOE_DN_FT2
-#define RMOE_DN_FT2 2
-#endif
 
 namespace rmoe {
 namespace {
@@ -71,9 +58,12 @@ constexpr int CHUNK_B = MF * CK * 2;  // 4 KB: one matrix's chunk
 // TT: 32-token tiles per pass: 1, 2 or 3 (96 tokens, the largest pass the
 // 160 KB of LDS holds); a block takes the narrowest pass that holds its rows,
 // so it reads its weights once instead of once per 32-token tile.
+// FT: 32-feature weight tiles per workgroup, the same for every pass width
+// (one grid serves them all): gate/up one (its gate and up rows; the wider
+// passes leave no LDS for a second), down two.
 template <bool DUAL, int KS, int D, int TT>
 struct StreamCfg {
-    static constexpr int FT = DUAL ? (TT == 1 ? RMOE_GU_FT1 : 1) : (TT == 1 ? RMOE_DN_FT1 : RMOE_DN_FT2);
+    static constexpr int FT = DUAL ? 1 : 2;
     static constexpr int G = DUAL ? 2 : 1;                  // matrices per feature tile: gate and up, or down
     static constexpr int NM = G * FT;                       // weight tiles: matrix g of feature tile f is g + G f
     static constexpr int SLOT = (NM + TT) * CHUNK_B;        // weights, then 32*TT token rows
