@@ -20,7 +20,7 @@ import torch
 
 import mixture_experts_routed_grouped_amd as R
 import workloads
-from _gpu_run import forward, prepare, untouched, valid_row_mask
+from _gpu_run import forward, fresh_outputs, prepare, untouched, valid_row_mask
 from _oracle_run import run as oracle_run
 from oracle import contract as C
 from oracle import combine as CB
@@ -94,6 +94,57 @@ def test_tiny(variant):
 def test_random_shapes(variant, seed, E, k, T, H, I, routing):
     cfg = workloads.Config(f"r{seed}", T, E, k, H, I, routing=routing, zipf_s=1.4, seed=seed)
     _full_compare(workloads.make_inputs(cfg), variant)
+
+
+def _sweep_configs(n=48, seed=2024):
+    """Seeded random batches for the sweep: expert counts 1-64, top-k up to
+    8, 1-400 tokens, H and I multiples of 128 up to 512, uniform or Zipf
+    routing (so group sizes land on every streaming pass plan and on lone,
+    full and multi-block tiled entries)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 401))
+        H = 128 * int(rng.integers(1, 5))
+        I = 128 * int(rng.integers(1, 5))
+        routing = "zipf" if rng.random() < 0.5 and E > 1 else "uniform"
+        out.append((100 + i, E, k, T, H, I, routing))
+    return out
+
+
+def test_random_shape_sweep():
+    """48 seeded random batches, each through both kernel families, AUTO and
+    the single-launch forward (both hand-overs), the whole padded output
+    against one oracle run: tables bit for bit, padding rows untouched, every
+    valid element within tolerance."""
+    for seed, E, k, T, H, I, routing in _sweep_configs():
+        cfg = workloads.Config(f"s{seed}", T, E, k, H, I, routing=routing, zipf_s=1.3, seed=seed)
+        inp = workloads.make_inputs(cfg)
+        print(f"[sweep] seed={seed} E={E} k={k} T={T} H={H} I={I} {routing}", flush=True)
+        orc = oracle_run(inp)
+        prow = np.asarray(orc["c"]["padded_row_of_pair"])
+        for variant in ("stream", "tile", "auto", "local", "global"):
+            d = prepare(inp)
+            if variant in ("local", "global"):
+                fresh_outputs(d)
+                sync = R.fused_sync(d["stacked"].device, d["gidx"].numel())
+                R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"],
+                                d["go"], d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync,
+                                handover=variant)
+                torch.cuda.synchronize()
+                assert R.fused_sync_errors(sync) == 0, "a down tile's wait timed out"
+            else:
+                forward(d, variant)
+            for key in ["group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx",
+                        "padded_row_of_pair"]:
+                assert np.asarray(d["c"][key]).tolist() == list(orc["c"][key]), key
+            mask = valid_row_mask(d)
+            assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
+            rows = d["prow"].long()
+            _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(),
+                           orc["hid"][prow], orc["out"][prow], f"sweep {seed}/{variant}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
