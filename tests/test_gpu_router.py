@@ -17,6 +17,7 @@ import mixture_experts_routed_grouped_amd as R
 import workloads
 from _oracle_run import run as oracle_run
 from oracle import combine as CB
+from oracle import contract as C
 from oracle import router as RT
 
 pytestmark = pytest.mark.gpu
@@ -110,3 +111,53 @@ def test_layer_from_gpu_router():
     ref_y = want.astype(np.float64)
     assert np.isfinite(got).all()
     assert (np.abs(got - ref_y) <= 2e-2 + 2e-2 * np.abs(ref_y)).all()
+
+
+def test_layer_sweep():
+    """16 seeded random layers (1-256 experts, top-k up to 8, 1-600 tokens,
+    H 128-512, I 128-256): the GPU router's top-k is a valid top-k of the
+    router oracle, the device contract built from it equals the contract
+    oracle's tables bit for bit, and router -> device contract -> pack ->
+    forward -> combine matches the oracle layer fed with the same routing."""
+    rng = np.random.default_rng(77)
+    dev = torch.device("cuda")
+    for i in range(16):
+        E = int(rng.integers(1, 257))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 601))
+        H = 128 * int(rng.integers(1, 5))
+        I = 128 * int(rng.integers(1, 3))
+        cfg = workloads.Config(f"ls{i}", T, E, k, H, I, seed=200 + i)
+        print(f"router: layer sweep {i}: T={T} E={E} k={k} H={H} I={I}", flush=True)
+        x = workloads._normal_f16((T, H), 1.0, cfg.seed, 1, "cpu")
+        wr = workloads.make_router_weight(cfg)
+        ids, vals = R.router(x.to(dev), wr.to(dev), k)
+        d = R.build_contract_device(ids, E)
+        torch.cuda.synchronize()
+        ids_h = ids.cpu().numpy()
+        _check_router(ids_h, vals.cpu().numpy(), x.numpy(), wr.numpy(), k)
+        oc = C.build_contract(ids_h.tolist(), E)
+        for key in ["group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx",
+                    "padded_row_of_pair", "compact_pos_of_pair"]:
+            assert d[key].cpu().numpy().tolist() == list(oc[key]), key
+        inp = workloads.make_inputs(cfg, topk_ids=ids_h)
+        inp.topk_w = vals.cpu().numpy()
+        inp.x = x
+        Tp = d["total_padded_tokens"]
+        stacked = torch.zeros((Tp, H), dtype=torch.float16, device=dev)
+        w_compact = torch.zeros(max(d["pairs"], 1), dtype=torch.float32, device=dev)
+        R.pack(x.to(dev), vals.reshape(-1), d["padded_row_of_pair"], d["compact_pos_of_pair"],
+               stacked, w_compact)
+        hid = torch.zeros((Tp, I), dtype=torch.float16, device=dev)
+        out = torch.zeros((Tp, H), dtype=torch.float16, device=dev)
+        R.forward(stacked, inp.wg.to(dev), inp.wu.to(dev), inp.wd.to(dev), w_compact[:d["pairs"]],
+                  d["group_sizes"], d["group_offsets"], d["group_padded_offsets"],
+                  d["group_idx_for_bx"], hid, out)
+        y = torch.empty((T, H), dtype=torch.float16, device=dev)
+        R.combine(out, d["padded_row_of_pair"], k, y)
+        torch.cuda.synchronize()
+        o = oracle_run(inp)
+        want = CB.combine(o["out"], np.asarray(o["c"]["padded_row_of_pair"]), T, k).astype(np.float64)
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        assert (np.abs(got - want) <= 2e-2 + 2e-2 * np.abs(want)).all(), f"layer sweep {i}"
