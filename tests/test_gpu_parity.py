@@ -36,7 +36,7 @@ def ulp16(v):
     return np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 10)
 
 
-def _assert_parity(gpu_hid, gpu_out, o_hid, o_out, what):
+def _assert_parity(gpu_hid, gpu_out, o_hid, o_out, what, ulp1_frac=0.01):
     gh, go_ = gpu_hid.astype(np.float64), gpu_out.astype(np.float64)
     oh, oo = o_hid.astype(np.float64), o_out.astype(np.float64)
     assert np.isfinite(gh).all() and np.isfinite(go_).all(), f"{what}: non-finite output"
@@ -47,7 +47,7 @@ def _assert_parity(gpu_hid, gpu_out, o_hid, o_out, what):
     u = ulp16(np.maximum(np.abs(gh), np.abs(oh)))
     over = dh > 2 * u + 3e-5
     assert not over.any(), f"{what}: {over.sum()} hidden entries beyond 2 ulps + 3e-5, max {dh.max()}"
-    assert np.count_nonzero(dh > u) <= 0.01 * dh.size, f"{what}: too many hidden entries > 1 ulp"
+    assert np.count_nonzero(dh > u) <= ulp1_frac * dh.size, f"{what}: too many hidden entries > 1 ulp"
     rel = np.sqrt((d ** 2).sum() / max((oo ** 2).sum(), 1e-30))
     assert rel < 2e-3, f"{what}: relative RMS error {rel}"
     return rel
@@ -145,6 +145,40 @@ def test_random_shape_sweep():
             rows = d["prow"].long()
             _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(),
                            orc["hid"][prow], orc["out"][prow], f"sweep {seed}/{variant}")
+
+
+@pytest.mark.parametrize("H,I", [(1 << 20, 128), (128, 1 << 20)])
+def test_maximum_hidden_and_intermediate(H, I):
+    """The largest H and I the entries accept (2^20 each): 64-bit row offsets,
+    K sweeps of 16384 chunks, 4096 or 8192 weight slices, the narrow last
+    down slice; both families, AUTO and the single launch, whole against the
+    oracle (two experts, three routed rows).  The stated bar (out within
+    2e-2 + 2e-2|oracle|) and the hidden bar of 2 ulps + 3e-5 hold as
+    everywhere; the share of hidden entries more than 1 ulp apart, a
+    diagnostic of the two sides' fp32 summation orders, grows with sqrt(K):
+    1% at the workloads' K (up to 14336) scales to about 9% at K = 2^20,
+    so it is bounded by 10% here."""
+    cfg = workloads.Config("maxdim", 3, 2, 1, H, I, seed=41)
+    inp = workloads.make_inputs(cfg, topk_ids=np.array([[0], [1], [1]], np.int32))
+    print(f"[max-dim] H={H} I={I}", flush=True)
+    orc = oracle_run(inp)
+    prow = np.asarray(orc["c"]["padded_row_of_pair"])
+    d = prepare(inp)
+    for variant in ("stream", "tile", "auto", "global"):
+        if variant == "global":
+            fresh_outputs(d)
+            sync = R.fused_sync(d["stacked"].device, d["gidx"].numel())
+            R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"], d["go"],
+                            d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, handover="global")
+            torch.cuda.synchronize()
+            assert R.fused_sync_errors(sync) == 0
+        else:
+            forward(d, variant)
+        mask = valid_row_mask(d)
+        assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
+        rows = d["prow"].long()
+        _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(), orc["hid"][prow],
+                       orc["out"][prow], f"max-dim H={H} I={I} {variant}", ulp1_frac=0.10)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
