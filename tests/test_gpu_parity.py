@@ -460,6 +460,32 @@ def test_stream_skewed_mid_batch(name, cfg):
     print(f"[stream-skew] {name}: {len(pairs)} rows within tolerance, rel RMS {rel:.2e}", flush=True)
 
 
+def test_maximum_blocks():
+    """The largest block table the entries accept (num_blocks_m = 65535, the
+    streaming grid's y limit): two experts share 8388224 tokens (k = 1,
+    H = I = 128).  Both families and AUTO: padding rows untouched and every
+    valid row written and finite over the whole buffers, one row of every
+    live block (plus each expert's first and last row) against the oracle."""
+    T = 65533 * 128
+    ids = workloads.routing_from_counts([T // 2, T - T // 2], seed=43)
+    cfg = workloads.Config("maxblocks", T, 2, 1, 128, 128, seed=43)
+    inp = workloads.make_inputs(cfg, topk_ids=ids)
+    print(f"[max-blocks] T={T}", flush=True)
+    d = prepare(inp)
+    assert d["c"]["num_blocks_m"] == 65535
+    pairs, blocks = _block_sample(d["c"], seed=9)
+    o_hid, o_out = _oracle_rows(inp, pairs)
+    mask = valid_row_mask(d)
+    sel = d["prow"][torch.tensor(pairs, device="cuda")].long()
+    for variant in ("stream", "tile", "auto"):
+        forward(d, variant)
+        assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
+        _all_valid_rows_written(d)
+        _assert_parity(d["hid"][sel].cpu().numpy(), d["out"][sel].cpu().numpy(), o_hid, o_out,
+                       f"max-blocks {variant}")
+    print(f"[max-blocks] {len(pairs)} rows of {blocks} live blocks within tolerance", flush=True)
+
+
 def test_pack_large_batch_nontemporal_path():
     """The large workload packs 1.9 GB of rows, above the size where pack
     stores them non-temporally: sampled rows equal their token's row bit for
