@@ -460,6 +460,37 @@ def test_stream_skewed_mid_batch(name, cfg):
     print(f"[stream-skew] {name}: {len(pairs)} rows within tolerance, rel RMS {rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("E", [8192, 65000])
+def test_many_experts(E):
+    """Many experts, nearly all of them empty (600 routed rows, top-2): every
+    empty expert still owns one slack block, so num_blocks_m is about E;
+    both families, AUTO and the single launch, whole against the oracle."""
+    cfg = workloads.Config(f"manyE{E}", 300, E, 2, 128, 128, seed=47)
+    inp = workloads.make_inputs(cfg, device="cuda")
+    inp.x, inp.wg, inp.wu, inp.wd = (t.cpu() for t in (inp.x, inp.wg, inp.wu, inp.wd))
+    print(f"[many-experts] E={E}", flush=True)
+    orc = oracle_run(inp)
+    prow = np.asarray(orc["c"]["padded_row_of_pair"])
+    d = prepare(inp)
+    for variant in ("stream", "tile", "auto", "global"):
+        if variant == "global":
+            fresh_outputs(d)
+            sync = R.fused_sync(d["stacked"].device, d["gidx"].numel())
+            R.forward_fused(d["stacked"], d["wg"], d["wu"], d["wd"], d["w_compact"], d["gs"], d["go"],
+                            d["gpo"], d["gidx"], d["hid"], d["out"], sync=sync, handover="global")
+            torch.cuda.synchronize()
+            assert R.fused_sync_errors(sync) == 0
+        else:
+            forward(d, variant)
+        for key in ["group_sizes", "group_offsets", "group_padded_offsets", "group_idx_for_bx"]:
+            assert np.asarray(d["c"][key]).tolist() == list(orc["c"][key]), key
+        mask = valid_row_mask(d)
+        assert untouched(d["hid"], mask) and untouched(d["out"], mask), "padding rows written"
+        rows = d["prow"].long()
+        _assert_parity(d["hid"][rows].cpu().numpy(), d["out"][rows].cpu().numpy(), orc["hid"][prow],
+                       orc["out"][prow], f"E={E} {variant}")
+
+
 def test_maximum_blocks():
     """The largest block table the entries accept (num_blocks_m = 65535, the
     streaming grid's y limit): two experts share 8388224 tokens (k = 1,
